@@ -1,0 +1,174 @@
+/*
+ * Reference oracle for one tensor-parallel rank's share of a Megatron MLP
+ * block.  TEST INFRASTRUCTURE ONLY: nothing on the product path may link,
+ * load or call this file.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark use it.
+ *
+ * Everything is plain fp64 C: straightforward loops, no BLAS, no blocking,
+ * no fast-math, floating-point contraction off.  Inputs are the exact fp64
+ * values of the (bf16- or fp32-rounded) host arrays the GPU receives.
+ * Matrices are the pages' logical ones, row-major:
+ *   X  [M][H]     activations
+ *   W1 [H][F]     up-projection,  Y = X W1   (W1 is [in][out])
+ *   b1 [F]        up-projection bias (optional)
+ *   W2 [F][H]     down-projection
+ * Shard i of T owns the contiguous column block C_i = [i*F/T, (i+1)*F/T)
+ * of W1 and the matching row block of W2.
+ *
+ * Sources (page title, then section):
+ *  [SLICE]  "Slice the matrix itself" (AI Engineering Visual Guide,
+ *           Tensor Parallelism scene): "Column-Parallel & Row-Parallel
+ *           GEMMs"; "Mathematical formulation - row-parallel matrix
+ *           multiplication summation".
+ *  [LESSON] "09. Tensor Parallelism in Action: Megatron-LM Matrix
+ *           Splitting across NVLink & NVSwitch Networks": section 1
+ *           (block split of W1 and W2, pipeline diagram), section 2,
+ *           question 2 (GeLU is elementwise, so it commutes with the
+ *           column split).
+ *  [GUIDE]  "Tensor parallelism" (inference guide): "Concept";
+ *           "Walking through a transformer block".
+ *  [GELU]   Hendrycks & Gimpel, "Gaussian Error Linear Units (GELUs)",
+ *           arXiv:1606.08415, the tanh approximation of x*Phi(x).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <omp.h>
+
+#define ORC_OK 0
+#define ORC_BAD_ARG 1
+
+/* GeLU, tanh form [GELU]:
+ *   g(x) = 0.5 * x * (1 + tanh( sqrt(2/pi) * (x + 0.044715 x^3) ))
+ * The pages name GeLU without a formula ([LESSON] section 1 diagram and
+ * section 2 question 2); the tanh form is the one the workloads specify. */
+static double gelu_tanh(double x)
+{
+    const double k = sqrt(2.0 / acos(-1.0));   /* sqrt(2/pi) */
+    return 0.5 * x * (1.0 + tanh(k * (x + 0.044715 * x * x * x)));
+}
+
+void orc_gelu(int64_t n, const double *x, double *y)
+{
+    for (int64_t j = 0; j < n; ++j)
+        y[j] = gelu_tanh(x[j]);
+}
+
+static int shard_ok(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i)
+{
+    return M >= 0 && H >= 1 && F >= 1 && T >= 1 && F % T == 0 && i >= 0 && i < T;
+}
+
+/* Column-parallel up-projection with bias and GeLU, shard i of T
+ * ([SLICE] column split Y_i = X W_i; [LESSON] W1 = [W1,1 | W1,2], no
+ * communication after the split; [GUIDE] "Concept": column-parallel shards
+ * W along the output dimension).
+ *   Y_i[m][c] = g( sum_{h=0}^{H-1} X[m][h] * W1[h][o+c]  +  b1[o+c] ),
+ *   o = i*F/T,  c in [0, F/T).
+ * The sum runs over h in increasing order and the bias is added last, for
+ * every element, so shard outputs equal the matching columns of the
+ * unsharded result bit for bit.  b1 may be NULL (no bias). */
+int orc_colpar_gelu(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i,
+                    const double *X, const double *W1, const double *b1,
+                    double *Y_i)
+{
+    if (!shard_ok(M, H, F, T, i) || !X || !W1 || !Y_i) return ORC_BAD_ARG;
+    const int64_t Fs = F / T, o = (int64_t)i * Fs;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double *acc = (double *)calloc((size_t)Fs, sizeof(double));
+        for (int64_t h = 0; h < H; ++h) {
+            const double x = X[m * H + h];
+            const double *w = W1 + h * F + o;
+            for (int64_t c = 0; c < Fs; ++c)
+                acc[c] += x * w[c];
+        }
+        for (int64_t c = 0; c < Fs; ++c) {
+            const double u = b1 ? acc[c] + b1[o + c] : acc[c];
+            Y_i[m * Fs + c] = gelu_tanh(u);
+        }
+        free(acc);
+    }
+    return ORC_OK;
+}
+
+/* Row-parallel partial product of shard i ([SLICE] Z = sum_i Y_i V_i and
+ * "row-parallel outputs are local partial sums"; [LESSON] W2 split into the
+ * row blocks [W2,1 ; W2,2]; [GUIDE] row-parallel shards W along the input
+ * dimension):
+ *   Z_i[m][n] = sum_{c=0}^{F/T-1} Y_i[m][c] * W2[o+c][n],   o = i*F/T.
+ * The same product with F := A (attention width) and Y_i := the rank's
+ * slice of the attention context gives the head-sharded output projection
+ * ([GUIDE] "Walking through a transformer block"). */
+int orc_rowpar_partial(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i,
+                       const double *Y_i, const double *W2, double *Z_i)
+{
+    if (!shard_ok(M, H, F, T, i) || !Y_i || !W2 || !Z_i) return ORC_BAD_ARG;
+    const int64_t Fs = F / T, o = (int64_t)i * Fs;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double *z = Z_i + m * H;
+        for (int64_t n = 0; n < H; ++n) z[n] = 0.0;
+        for (int64_t c = 0; c < Fs; ++c) {
+            const double y = Y_i[m * Fs + c];
+            const double *w = W2 + (o + c) * H;
+            for (int64_t n = 0; n < H; ++n)
+                z[n] += y * w[n];
+        }
+    }
+    return ORC_OK;
+}
+
+/* Sum of the T row-parallel partials: what the All-Reduce-Sum delivers to
+ * every rank ([SLICE] summation formula; [LESSON] one all-reduce completes
+ * the MLP).  Optionally the residual stream is added ([GUIDE] both
+ * all-reduces sit on residual paths):
+ *   out[m][n] = (residual ? residual[m][n] : 0) + sum_{j=0}^{T-1} P_j[m][n]
+ * with partials laid out [T][M][H].
+ * rms_out (optional, not from the pages): the row-normalised copy
+ *   rms_out[m][n] = out[m][n] / sqrt( mean_n out[m][n]^2 + eps )
+ * used to keep a deep stack of blocks with no normalisation layer finite. */
+int orc_shard_reduce(int32_t T, int64_t M, int64_t H, const double *partials,
+                     const double *residual, double *out, double *rms_out,
+                     double eps)
+{
+    if (T < 1 || M < 0 || H < 1 || !partials || !out) return ORC_BAD_ARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < H; ++n) {
+            double s = 0.0;
+            for (int32_t j = 0; j < T; ++j)
+                s += partials[((int64_t)j * M + m) * H + n];
+            out[m * H + n] = residual ? residual[m * H + n] + s : s;
+        }
+        if (rms_out) {
+            double ss = 0.0;
+            for (int64_t n = 0; n < H; ++n)
+                ss += out[m * H + n] * out[m * H + n];
+            const double r = 1.0 / sqrt(ss / (double)H + eps);
+            for (int64_t n = 0; n < H; ++n)
+                rms_out[m * H + n] = out[m * H + n] * r;
+        }
+    }
+    return ORC_OK;
+}
+
+/* The unsharded MLP the shards reconstruct ([LESSON] pipeline diagram:
+ * input, W1, GeLU, W2):  Y = g(X W1 + b1),  Z = Y W2.
+ * Y [M][F] and Z [M][H] are outputs; Y may be NULL only if not wanted. */
+int orc_mlp_unsharded(int64_t M, int64_t H, int64_t F,
+                      const double *X, const double *W1, const double *b1,
+                      const double *W2, double *Y, double *Z)
+{
+    if (M < 0 || H < 1 || F < 1 || !X || !W1 || !W2 || !Z) return ORC_BAD_ARG;
+    double *y = Y ? Y : (double *)malloc((size_t)(M > 0 ? M : 1) * (size_t)F * sizeof(double));
+    if (!y) return ORC_BAD_ARG;
+    int rc = orc_colpar_gelu(M, H, F, 1, 0, X, W1, b1, y);
+    if (rc == ORC_OK) rc = orc_rowpar_partial(M, H, F, 1, 0, y, W2, Z);
+    if (!Y) free(y);
+    return rc;
+}
+
+void orc_set_threads(int32_t n) { if (n > 0) omp_set_num_threads(n); }
+int32_t orc_max_threads(void) { return (int32_t)omp_get_max_threads(); }
