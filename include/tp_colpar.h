@@ -1,0 +1,175 @@
+/*
+ * tp_colpar.h -- one tensor-parallel rank's share of a Megatron MLP block on
+ * MI355X (gfx950): the column-parallel up-projection with fused bias + GeLU,
+ * the row-parallel down-projection (and the head-sharded attention output
+ * projection) that yields an fp32 partial sum, and the on-device sum of the
+ * T partials that stands in for the cross-GPU All-Reduce-Sum.
+ *
+ * Sources (page title, then section):
+ *  [SLICE]  "Slice the matrix itself" (AI Engineering Visual Guide, Tensor
+ *           Parallelism scene): "Column-Parallel & Row-Parallel GEMMs",
+ *           "All-Reduce Synchronization", "Mathematical formulation -
+ *           row-parallel matrix multiplication summation".
+ *  [LESSON] "09. Tensor Parallelism in Action: Megatron-LM Matrix Splitting
+ *           across NVLink & NVSwitch Networks": section 1 (W1 split by
+ *           columns, W2 by rows, one all-reduce, the pipeline diagram),
+ *           section 2 question 2 (GeLU commutes with the column split).
+ *  [GUIDE]  "Tensor parallelism" (inference guide): "Concept", "Walking
+ *           through a transformer block".
+ *  [GELU]   Hendrycks & Gimpel, arXiv:1606.08415 (tanh form of GeLU).
+ *
+ * Notation: M tokens, hidden size H, FFN width F, TP degree T, shard index
+ * i in [0, T) (the pages count ranks from 1), shard width Fs = F/T, column
+ * block C_i = [i*Fs, (i+1)*Fs).  Logical weights are the pages' [in][out]
+ * matrices (Y = X W).  They are STORED K-CONTIGUOUS, i.e. transposed:
+ *   W1t = W1^T, row-major [F][H]   (row f holds column f of W1)
+ *   W2t = W2^T, row-major [H][F]   (row h holds column h of W2)
+ * All activations are row-major: X [M][H], Y_i [M][Fs], Z_i [M][H].
+ *
+ * Precision (tp_dtype):
+ *   TP_BF16: X, W1t, b1, W2t, Y_i are bf16; products accumulate in fp32;
+ *            partials Z_i and the reduction are fp32.
+ *   TP_F32:  every tensor is fp32, fp32 arithmetic throughout.
+ *
+ * Ownership: the caller allocates, owns and frees every buffer (device
+ * memory on the current HIP device, except the host array of partial
+ * pointers of tp_shard_reduce).  The library allocates nothing, frees
+ * nothing and never synchronizes; all work is enqueued on `stream`.
+ *
+ * Errors: every entry point validates its arguments on the host BEFORE any
+ * HIP call and returns a tp_status; TP_ERR_HIP reports a failed launch.
+ * TP_OK means "enqueued": a device fault surfaces at the caller's next
+ * synchronization.  tp_last_error() gives a message for the calling thread's
+ * last non-OK status.  Nothing throws or aborts across this boundary.
+ *
+ * Common validation (in this order):
+ *   M >= 0, H >= 1, F >= 1, 1 <= T <= TP_MAX_T, F % T == 0, 0 <= i < T
+ *                                                     -> TP_ERR_SHAPE
+ *   required pointers non-NULL                        -> TP_ERR_NULL
+ *   dtype known, H % 64 == 0, Fs % 64 == 0, every pointer 16-byte aligned
+ *                                                     -> TP_ERR_UNSUPPORTED
+ *   an output overlapping an input                    -> TP_ERR_ALIAS
+ * M == 0 is a valid empty call: TP_OK, nothing enqueued, nothing touched.
+ */
+#ifndef TP_COLPAR_H
+#define TP_COLPAR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_NULL = 1,         /* a required pointer is NULL                  */
+    TP_ERR_SHAPE = 2,        /* sizes or shard index out of range           */
+    TP_ERR_UNSUPPORTED = 3,  /* valid but not supported: dtype, alignment,
+                                H or F/T not a multiple of 64               */
+    TP_ERR_HIP = 4,          /* a HIP call failed (message has the reason)  */
+    TP_ERR_ALIAS = 5         /* an output overlaps an input                 */
+} tp_status;
+
+typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
+
+/* Largest TP degree: TP stays inside one 8-GPU node ([SLICE] "Strict
+ * NVLink Domain Constraint"; [GUIDE] "Trade-off"). */
+#define TP_MAX_T 8
+
+/* tp_shard_reduce flag: also write out_bf16 = out_f32 / rms(out_f32) per row
+ * (rms = sqrt(mean of squares + TP_RMS_EPS)).  Not from the pages: it keeps
+ * a deep stack of blocks that has no normalisation layer finite. */
+#define TP_REDUCE_RMS_BF16 1u
+#define TP_RMS_EPS 1e-6f
+
+/*
+ * Column-parallel up-projection, bias and GeLU of shard i ([SLICE]
+ * "Column-Parallel & Row-Parallel GEMMs"; [LESSON] section 1, no
+ * communication after the column split; [LESSON] section 2 question 2: GeLU
+ * is elementwise, so it is applied to the shard with no sync; [GELU]):
+ *
+ *   Y_i[m][c] = g( sum_h X[m][h] * W1t[i*Fs + c][h] + b1[i*Fs + c] )
+ *   g(u) = u/2 * (1 + tanh( sqrt(2/pi) * (u + 0.044715 u^3) ))
+ *
+ *   X    [M][H]   input                                  (dtype)
+ *   W1t  [F][H]   full W1^T; rows C_i are read           (dtype)
+ *   b1   [F]      full bias; entries C_i are read; NULL = no bias (dtype)
+ *   Y_i  [M][Fs]  output, written                        (dtype)
+ * bf16: products in fp32, bias and GeLU in fp32, Y_i rounded to bf16
+ * (round to nearest even).  Rank-local weights: pass the shard as the whole
+ * matrix with F := Fs, T = 1, i = 0.
+ */
+tp_status tp_colpar_gelu(const void *X, const void *W1t, const void *b1, void *Y_i,
+                         int64_t M, int64_t H, int64_t F, int32_t T, int32_t i,
+                         tp_dtype dt, hipStream_t stream);
+
+/*
+ * Row-parallel partial product of shard i ([SLICE] "Column-Parallel &
+ * Row-Parallel GEMMs" and the row-parallel summation: each rank's output is
+ * a local partial sum; [LESSON] section 1, W2 split by rows; [GUIDE]
+ * "Concept"):
+ *
+ *   Z_i[m][n] = sum_c Y_i[m][c] * W2t[n][i*Fs + c]
+ *
+ *   Y_i  [M][Fs]  input                                  (dtype)
+ *   W2t  [H][F]   full W2^T; columns C_i are read (row stride F) (dtype)
+ *   Z_i  [M][H]   partial, written, always fp32
+ * The head-sharded attention output projection ([GUIDE] "Walking through a
+ * transformer block": heads are split across ranks) is the same call with
+ * Y_i := ctx_i [M][A/T] (the rank's heads, contiguous), W2t := W_o^T [H][A]
+ * and F := A.
+ */
+tp_status tp_rowpar_partial(const void *Y_i, const void *W2t, float *Z_i,
+                            int64_t M, int64_t H, int64_t F, int32_t T, int32_t i,
+                            tp_dtype dt, hipStream_t stream);
+
+/*
+ * Sum of the T row-parallel partials: on one GPU this stands in for the
+ * All-Reduce-Sum that completes each row-parallel projection ([SLICE]
+ * summation formula and "All-Reduce Synchronization"; [LESSON] section 1:
+ * one all-reduce completes the MLP; [GUIDE] the all-reduces sit on the
+ * residual paths):
+ *
+ *   s = partials[0] + partials[1] + ... + partials[T-1]   (this order, fp32)
+ *   out_f32 = residual ? residual + s : s
+ *   out_bf16 (optional) = bf16(out_f32), or with TP_REDUCE_RMS_BF16
+ *                         bf16(out_f32 / sqrt(mean_row(out_f32^2) + TP_RMS_EPS))
+ *
+ *   partials  HOST array of T device pointers, each [M][H] fp32
+ *   residual  [M][H] fp32 or NULL; out_f32 may be the same buffer
+ *   out_f32   [M][H] fp32, written
+ *   out_bf16  [M][H] bf16 or NULL (required with TP_REDUCE_RMS_BF16)
+ * Validation: 1 <= T <= TP_MAX_T, M >= 0, H >= 1 (TP_ERR_SHAPE); partials,
+ * each partials[j], out_f32 non-NULL (TP_ERR_NULL); H % 4 == 0, 16-byte
+ * aligned pointers, known flags (TP_ERR_UNSUPPORTED); outputs overlapping a
+ * partial, or out_bf16 overlapping anything (TP_ERR_ALIAS).
+ * Deterministic: fixed order, no atomics.
+ */
+tp_status tp_shard_reduce(const float *const *partials, int32_t T, const float *residual,
+                          float *out_f32, void *out_bf16, int64_t M, int64_t H,
+                          uint32_t flags, hipStream_t stream);
+
+/*
+ * Rank i's whole MLP share ([LESSON] section 1 pipeline: input, column-
+ * parallel W1, GeLU, row-parallel W2, then the all-reduce): tp_colpar_gelu
+ * into the caller's workspace Y_ws [M][Fs], then tp_rowpar_partial into
+ * Z_i [M][H] fp32.  Same arguments and validation as the two calls; Y_ws
+ * must not overlap any other buffer.  In bf16, M <= 32 takes the
+ * weight-streaming decode kernels, larger M the MFMA GEMM kernels.
+ */
+tp_status tp_mlp_shard_fwd(const void *X, const void *W1t, const void *b1, const void *W2t,
+                           void *Y_ws, float *Z_i, int64_t M, int64_t H, int64_t F,
+                           int32_t T, int32_t i, tp_dtype dt, hipStream_t stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *tp_last_error(void);
+
+/* Library version string. */
+const char *tp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_COLPAR_H */

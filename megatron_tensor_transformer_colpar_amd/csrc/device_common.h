@@ -1,0 +1,64 @@
+// Device helpers shared by the HIP kernels: vector types, buffer resources,
+// the GeLU epilogue and the workgroup -> tile mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource over [base, base + bytes): loads at or past the end return
+// zero, which makes ragged tiles free.  Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+
+// GeLU, tanh form (Hendrycks & Gimpel, arXiv:1606.08415):
+//   g(x) = x/2 * (1 + tanh(u)),  u = sqrt(2/pi) * (x + 0.044715 x^3).
+// Evaluated through (1 + tanh u)/2 = 1/(1 + exp(-2u)), so one exp and one
+// reciprocal; exp comes from the device library.  The limits are right:
+// x -> -inf gives exp -> inf and g -> -0; x -> +inf gives g -> x.
+__device__ __forceinline__ float gelu_tanh(float x)
+{
+    const float two_k = 1.5957691216057308f;  // 2 * sqrt(2/pi)
+    const float v = two_k * x * (1.0f + 0.044715f * x * x);
+    return __fdividef(x, 1.0f + __expf(-v));
+}
+
+// Workgroup id -> (tile_m, tile_n).  Consecutive workgroup ids are dealt
+// round-robin to the 8 XCDs, each with its own L2; this remap gives every XCD
+// a contiguous run of logical tiles, and walks the logical tiles in groups of
+// GROUP_M tile-rows so the tiles in flight on one XCD share A and B panels.
+template <int GROUP_M>
+__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int total = tiles_m * tiles_n;
+    int logical = bid;
+    if ((total & 7) == 0) {
+        const int per_xcd = total >> 3;
+        logical = (bid & 7) * per_xcd + (bid >> 3);
+    }
+    const int per_group = GROUP_M * tiles_n;
+    const int group = logical / per_group;
+    const int first_m = group * GROUP_M;
+    const int gsize = min(tiles_m - first_m, GROUP_M);
+    const int r = logical - group * per_group;
+    tm = first_m + r % gsize;
+    tn = r / gsize;
+}
+
+}  // namespace tpk

@@ -1,0 +1,139 @@
+// bf16 skinny-M path (decode, M <= 32):
+//   C[m][n] = sum_k X[m][k] * W[n][k]
+// At decode the weights are read once and the tokens are few, so the kernel
+// is a weight stream: it is bound by HBM bandwidth, and the few tokens ride
+// along in MFMA tiles padded to 16 tokens (the MFMA units have orders of
+// magnitude of headroom at this intensity, VALU would not at M = 32).
+//
+// Layout: a workgroup owns 16 weight rows [n0, n0+16) and KS waves; wave w
+// streams the K range [w*K/KS, (w+1)*K/KS) of those rows with 16-byte loads
+// (16 rows x 64 contiguous bytes per load instruction) and multiplies them
+// with v_mfma_f32_16x16x32_bf16 against 16-token tiles of X (tokens past M
+// read as zero through the buffer resource).  The KS partial tiles are then
+// summed in LDS in fixed order (deterministic, no atomics) and the epilogue
+// (bias + GeLU -> bf16, or fp32) is applied.
+#include "device_common.h"
+#include "tp_kernels.h"
+
+namespace tpk {
+namespace {
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+struct GemvDev {
+    const __bf16 *X;
+    const __bf16 *W;
+    const __bf16 *bias;
+    void *C;
+    int64_t ldx, ldw, ldc;
+    int M, N, K;
+};
+
+template <int EPI, int MT, int KS, int U>
+__global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
+{
+    __shared__ float red[KS][MT * 4 * 64];
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int Kw = g.K / KS;
+    const int kbeg = w * Kw;
+
+    const __amdgpu_buffer_rsrc_t wsrc =
+        make_rsrc(g.W + (int64_t)n0 * g.ldw, (uint32_t)(16 * g.ldw * 2));
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(g.X, (uint32_t)((int64_t)g.M * g.ldx * 2));
+
+    // lane geometry of the 16x16x32 MFMA operands: row (lane & 15), K chunk
+    // (lane >> 4) of 8 elements
+    const int r16 = lane & 15, kq = (lane >> 4) * 8;
+    const uint32_t w_voff = (uint32_t)((r16 * g.ldw + kbeg + kq) * 2);
+    uint32_t x_voff[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) x_voff[mt] = (uint32_t)(((mt * 16 + r16) * g.ldx + kbeg + kq) * 2);
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{};
+
+    for (int k = 0; k < Kw; k += 32 * U) {
+        u32x4 wv[U], xv[U][MT];
+        const uint32_t soff = (uint32_t)k * 2;
+#pragma unroll
+        for (int u = 0; u < U; ++u) wv[u] = buf_load16(wsrc, w_voff + u * 64, soff);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) xv[u][mt] = buf_load16(xsrc, x_voff[mt] + u * 64, soff);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, wv[u]),
+                                                                   __builtin_bit_cast(bf16x8v, xv[u][mt]),
+                                                                   acc[mt], 0, 0, 0);
+    }
+
+    // accumulator element v of token tile mt: weight row 4*(lane/16) + v,
+    // token mt*16 + lane%16
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[w][(mt * 4 + v) * 64 + lane] = acc[mt][v];
+    __syncthreads();
+
+    for (int idx = t; idx < MT * 4 * 64; idx += KS * 64) {
+        float s = red[0][idx];
+#pragma unroll
+        for (int j = 1; j < KS; ++j) s += red[j][idx];
+        const int l = idx & 63, v = (idx >> 6) & 3, mt = idx >> 8;
+        const int m = mt * 16 + (l & 15);
+        const int n = n0 + 4 * (l >> 4) + v;
+        if (m >= g.M) continue;
+        if (EPI == EPI_BIAS_GELU) {
+            const float b = g.bias ? (float)g.bias[n] : 0.0f;
+            static_cast<__bf16 *>(g.C)[(int64_t)m * g.ldc + n] = (__bf16)gelu_tanh(s + b);
+        } else {
+            static_cast<float *>(g.C)[(int64_t)m * g.ldc + n] = s;
+        }
+    }
+}
+
+template <int EPI, int MT>
+hipError_t launch_mt(const GemvDev &g, hipStream_t s)
+{
+    const dim3 grid((unsigned)(g.N / 16));
+    // Split K over as many waves as keeps >= 128 elements per wave and a
+    // 128-element (U = 4) or 64-element (U = 2) inner step.
+    if (g.K % (8 * 128) == 0)
+        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, 8, 4>), grid, dim3(8 * 64), 0, s, g);
+    else if (g.K % (4 * 128) == 0)
+        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, 4, 4>), grid, dim3(4 * 64), 0, s, g);
+    else if (g.K % (2 * 128) == 0)
+        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, 2, 4>), grid, dim3(2 * 64), 0, s, g);
+    else
+        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, 1, 2>), grid, dim3(64), 0, s, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int /*num_cu*/, hipStream_t s)
+{
+    GemvDev g;
+    g.X = static_cast<const __bf16 *>(a.A);
+    g.W = static_cast<const __bf16 *>(a.B);
+    g.bias = static_cast<const __bf16 *>(a.bias);
+    g.C = a.C;
+    g.ldx = a.lda;
+    g.ldw = a.ldb;
+    g.ldc = a.ldc;
+    g.M = (int)a.M;
+    g.N = (int)a.N;
+    g.K = (int)a.K;
+    const bool two = a.M > 16;
+    if (epi == EPI_BIAS_GELU)
+        return two ? launch_mt<EPI_BIAS_GELU, 2>(g, s) : launch_mt<EPI_BIAS_GELU, 1>(g, s);
+    return two ? launch_mt<EPI_STORE_F32, 2>(g, s) : launch_mt<EPI_STORE_F32, 1>(g, s);
+}
+
+}  // namespace tpk

@@ -1,0 +1,113 @@
+// Sum of the T row-parallel partials (the on-device stand-in for the
+// All-Reduce-Sum), with the optional residual add and bf16 copy:
+//   s = P_0 + P_1 + ... + P_{T-1}   (fixed order, fp32)
+//   out = residual ? residual + s : s
+//   out_bf16 = bf16(out)  or  bf16(out / sqrt(mean_row(out^2) + eps))
+// Pure streaming: (T + 1 [+1]) * 4 bytes read and 4 [+2] written per element,
+// so it is HBM-bound.  Every lane moves 16 bytes per tensor per step, and all
+// T loads of a step are issued before the adds.  The row-normalised variant
+// runs one workgroup per row and reduces the sum of squares with wavefront
+// shuffles, then across the four waves through LDS.
+#include "device_common.h"
+#include "tp_kernels.h"
+
+namespace tpk {
+namespace {
+
+struct PartialPtrs {
+    const f32x4 *p[kMaxPartials];
+};
+
+__device__ __forceinline__ u32x2 pack_bf16x4(f32x4 v)
+{
+    const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    return __builtin_bit_cast(u32x2, b);
+}
+
+template <int T>
+__device__ __forceinline__ f32x4 sum_partials(const PartialPtrs &P, int64_t i)
+{
+    f32x4 v[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) v[j] = P.p[j][i];
+    f32x4 s = v[0];
+#pragma unroll
+    for (int j = 1; j < T; ++j) s += v[j];
+    return s;
+}
+
+template <int T>
+__global__ void __launch_bounds__(256) reduce_kernel(PartialPtrs P, const f32x4 *residual, f32x4 *out,
+                                                     u32x2 *out_bf16, int64_t n4)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        f32x4 s = sum_partials<T>(P, i);
+        if (residual) s = residual[i] + s;
+        out[i] = s;
+        if (out_bf16) out_bf16[i] = pack_bf16x4(s);
+    }
+}
+
+template <int T>
+__global__ void __launch_bounds__(256) reduce_rms_kernel(PartialPtrs P, const f32x4 *residual, f32x4 *out,
+                                                         u32x2 *out_bf16, int64_t h4, float inv_h, float eps)
+{
+    __shared__ float wsum[4];
+    const int64_t base = (int64_t)blockIdx.x * h4;
+    float ss = 0.0f;
+    for (int64_t c = threadIdx.x; c < h4; c += 256) {
+        f32x4 s = sum_partials<T>(P, base + c);
+        if (residual) s = residual[base + c] + s;
+        out[base + c] = s;
+        ss += s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    const float r = rsqrtf(tot * inv_h + eps);
+    // each thread re-reads only the elements it wrote itself
+    for (int64_t c = threadIdx.x; c < h4; c += 256) out_bf16[base + c] = pack_bf16x4(out[base + c] * r);
+}
+
+template <int T>
+hipError_t launch_t(const PartialPtrs &P, const float *residual, float *out, void *ob, int64_t M,
+                    int64_t H, bool rms, float eps, hipStream_t s)
+{
+    const f32x4 *r4 = reinterpret_cast<const f32x4 *>(residual);
+    f32x4 *o4 = reinterpret_cast<f32x4 *>(out);
+    u32x2 *b4 = static_cast<u32x2 *>(ob);
+    if (rms) {
+        hipLaunchKernelGGL(reduce_rms_kernel<T>, dim3((unsigned)M), dim3(256), 0, s, P, r4, o4, b4, H / 4,
+                           1.0f / (float)H, eps);
+    } else {
+        const int64_t n4 = M * H / 4;
+        const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 1 << 16);
+        hipLaunchKernelGGL(reduce_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, P, r4, o4, b4, n4);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_shard_reduce(const float *const *partials, int T, const float *residual, float *out,
+                               void *out_bf16, int64_t M, int64_t H, bool rms, float eps, hipStream_t s)
+{
+    PartialPtrs P{};
+    for (int j = 0; j < T; ++j) P.p[j] = reinterpret_cast<const f32x4 *>(partials[j]);
+    switch (T) {
+    case 1: return launch_t<1>(P, residual, out, out_bf16, M, H, rms, eps, s);
+    case 2: return launch_t<2>(P, residual, out, out_bf16, M, H, rms, eps, s);
+    case 3: return launch_t<3>(P, residual, out, out_bf16, M, H, rms, eps, s);
+    case 4: return launch_t<4>(P, residual, out, out_bf16, M, H, rms, eps, s);
+    case 5: return launch_t<5>(P, residual, out, out_bf16, M, H, rms, eps, s);
+    case 6: return launch_t<6>(P, residual, out, out_bf16, M, H, rms, eps, s);
+    case 7: return launch_t<7>(P, residual, out, out_bf16, M, H, rms, eps, s);
+    case 8: return launch_t<8>(P, residual, out, out_bf16, M, H, rms, eps, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tpk

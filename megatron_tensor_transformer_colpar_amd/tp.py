@@ -1,0 +1,110 @@
+"""ctypes binding of libtpcolpar.so: argument marshalling only.
+
+The functions carry the C names and argument order of ``include/tp_colpar.h``.
+Tensor arguments may be torch tensors (their ``data_ptr()`` is passed), plain
+integer addresses, or None for NULL.  ``stream=None`` means torch's current
+stream on the current device.  A non-OK status raises ``TPError`` carrying the
+status and the library's message; the ``raw`` attribute exposes the C functions
+for callers that want the status code itself.
+
+Importing this module raises if the library has not been built: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtpcolpar.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libtpcolpar.so is not built (%s); build it with "
+        "`python -m megatron_tensor_transformer_colpar_amd.build`" % LIB_PATH)
+
+raw = ctypes.CDLL(LIB_PATH)
+
+TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_UNSUPPORTED, TP_ERR_HIP, TP_ERR_ALIAS = range(6)
+STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_UNSUPPORTED",
+                4: "TP_ERR_HIP", 5: "TP_ERR_ALIAS"}
+TP_BF16, TP_F32 = 0, 1
+TP_REDUCE_RMS_BF16 = 1
+TP_RMS_EPS = 1e-6
+TP_MAX_T = 8
+
+_vp, _i64, _i32, _u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+raw.tp_colpar_gelu.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+raw.tp_rowpar_partial.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+raw.tp_shard_reduce.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _i64, _i64, _u32, _vp]
+raw.tp_mlp_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+for _f in (raw.tp_colpar_gelu, raw.tp_rowpar_partial, raw.tp_shard_reduce, raw.tp_mlp_shard_fwd):
+    _f.restype = ctypes.c_int
+raw.tp_last_error.argtypes = []
+raw.tp_last_error.restype = ctypes.c_char_p
+raw.tp_version.argtypes = []
+raw.tp_version.restype = ctypes.c_char_p
+
+EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_shard_fwd",
+           "tp_last_error", "tp_version")
+
+
+class TPError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), message))
+        self.status = status
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st: int):
+    if st != TP_OK:
+        raise TPError(st, last_error())
+
+
+def last_error() -> str:
+    return raw.tp_last_error().decode()
+
+
+def version() -> str:
+    return raw.tp_version().decode()
+
+
+def tp_colpar_gelu(X, W1t, b1, Y_i, M, H, F, T, i, dt=TP_BF16, stream=None):
+    _check(raw.tp_colpar_gelu(_ptr(X), _ptr(W1t), _ptr(b1), _ptr(Y_i), M, H, F, T, i, dt, _stream(stream)))
+
+
+def tp_rowpar_partial(Y_i, W2t, Z_i, M, H, F, T, i, dt=TP_BF16, stream=None):
+    _check(raw.tp_rowpar_partial(_ptr(Y_i), _ptr(W2t), _ptr(Z_i), M, H, F, T, i, dt, _stream(stream)))
+
+
+def partial_array(partials):
+    """Host array of device pointers for tp_shard_reduce."""
+    return (_vp * len(partials))(*[_ptr(p) for p in partials])
+
+
+def tp_shard_reduce(partials, T, residual, out_f32, out_bf16, M, H, flags=0, stream=None):
+    arr = partials if isinstance(partials, ctypes.Array) else partial_array(partials)
+    _check(raw.tp_shard_reduce(arr, T, _ptr(residual), _ptr(out_f32), _ptr(out_bf16), M, H, flags,
+                               _stream(stream)))
+
+
+def tp_mlp_shard_fwd(X, W1t, b1, W2t, Y_ws, Z_i, M, H, F, T, i, dt=TP_BF16, stream=None):
+    _check(raw.tp_mlp_shard_fwd(_ptr(X), _ptr(W1t), _ptr(b1), _ptr(W2t), _ptr(Y_ws), _ptr(Z_i), M, H, F,
+                                T, i, dt, _stream(stream)))

@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and every invalid argument is rejected with the documented
+status before any HIP call (so these run on a machine without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from megatron_tensor_transformer_colpar_amd import tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_colpar.h")
+
+BF16, F32 = tp.TP_BF16, tp.TP_F32
+# Fake, 16-byte aligned device addresses far apart: validation never
+# dereferences them and a rejected call makes no HIP call.
+P = [0x10000000 * (k + 1) for k in range(12)]
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:tp_status|const char \*)\s*(tp_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(tp.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tp.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in tp.version()
+
+
+def colpar(X=P[0], W=P[1], b=P[2], Y=P[3], M=4, H=64, F=256, T=4, i=0, dt=BF16):
+    return tp.raw.tp_colpar_gelu(X, W, b, Y, M, H, F, T, i, dt, None)
+
+
+def rowpar(Y=P[3], W=P[4], Z=P[5], M=4, H=64, F=256, T=4, i=0, dt=BF16):
+    return tp.raw.tp_rowpar_partial(Y, W, Z, M, H, F, T, i, dt, None)
+
+
+def mlp(X=P[0], W1=P[1], b=P[2], W2=P[4], Y=P[3], Z=P[5], M=4, H=64, F=256, T=4, i=0, dt=BF16):
+    return tp.raw.tp_mlp_shard_fwd(X, W1, b, W2, Y, Z, M, H, F, T, i, dt, None)
+
+
+def reduce(parts=None, T=2, res=None, out=P[8], ob=None, M=4, H=64, flags=0):
+    parts = [P[6], P[7]] if parts is None else parts
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts) if parts else None
+    return tp.raw.tp_shard_reduce(arr, T, res, out, ob, M, H, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), tp.TP_ERR_SHAPE),
+    (dict(M=2**31), tp.TP_ERR_SHAPE),
+    (dict(H=0), tp.TP_ERR_SHAPE),
+    (dict(F=0), tp.TP_ERR_SHAPE),
+    (dict(T=0), tp.TP_ERR_SHAPE),
+    (dict(T=9, F=64 * 9), tp.TP_ERR_SHAPE),
+    (dict(F=250), tp.TP_ERR_SHAPE),
+    (dict(i=-1), tp.TP_ERR_SHAPE),
+    (dict(i=4), tp.TP_ERR_SHAPE),
+    (dict(X=None), tp.TP_ERR_NULL),
+    (dict(W=None), tp.TP_ERR_NULL),
+    (dict(Y=None), tp.TP_ERR_NULL),
+    (dict(dt=7), tp.TP_ERR_UNSUPPORTED),
+    (dict(H=96), tp.TP_ERR_UNSUPPORTED),
+    (dict(F=4 * 96), tp.TP_ERR_UNSUPPORTED),
+    (dict(H=2**23), tp.TP_ERR_UNSUPPORTED),
+    (dict(X=P[0] + 8), tp.TP_ERR_UNSUPPORTED),
+    (dict(b=P[2] + 2), tp.TP_ERR_UNSUPPORTED),
+    (dict(Y=P[0] + 64), tp.TP_ERR_ALIAS),
+    (dict(Y=P[1] + 4096), tp.TP_ERR_ALIAS),
+])
+def test_colpar_rejects(kw, status):
+    assert colpar(**kw) == status
+    assert "tp_colpar_gelu" in tp.last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-5), tp.TP_ERR_SHAPE),
+    (dict(T=3), tp.TP_ERR_SHAPE),          # 256 % 3
+    (dict(i=7), tp.TP_ERR_SHAPE),
+    (dict(Z=None), tp.TP_ERR_NULL),
+    (dict(W=None), tp.TP_ERR_NULL),
+    (dict(dt=2), tp.TP_ERR_UNSUPPORTED),
+    (dict(Z=P[5] + 4), tp.TP_ERR_UNSUPPORTED),
+    (dict(Z=P[3]), tp.TP_ERR_ALIAS),
+    (dict(Z=P[4] + 1024), tp.TP_ERR_ALIAS),
+])
+def test_rowpar_rejects(kw, status):
+    assert rowpar(**kw) == status
+    assert "tp_rowpar_partial" in tp.last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Y=None), tp.TP_ERR_NULL),
+    (dict(W2=None), tp.TP_ERR_NULL),
+    (dict(Z=P[0]), tp.TP_ERR_ALIAS),        # Z over X
+    (dict(Z=P[2]), tp.TP_ERR_ALIAS),        # Z over b1
+    (dict(Y=P[4]), tp.TP_ERR_ALIAS),        # workspace over W2t
+    (dict(Y=P[5]), tp.TP_ERR_ALIAS),        # workspace over Z
+])
+def test_mlp_shard_rejects(kw, status):
+    assert mlp(**kw) == status
+    assert "tp_mlp_shard_fwd" in tp.last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), tp.TP_ERR_SHAPE),
+    (dict(T=9, parts=[P[6]] * 9), tp.TP_ERR_SHAPE),
+    (dict(M=-1), tp.TP_ERR_SHAPE),
+    (dict(H=0), tp.TP_ERR_SHAPE),
+    (dict(parts=[], T=2), tp.TP_ERR_NULL),
+    (dict(parts=[P[6], None]), tp.TP_ERR_NULL),
+    (dict(out=None), tp.TP_ERR_NULL),
+    (dict(flags=1), tp.TP_ERR_NULL),         # RMS copy needs out_bf16
+    (dict(flags=2, ob=P[9]), tp.TP_ERR_UNSUPPORTED),
+    (dict(H=66), tp.TP_ERR_UNSUPPORTED),
+    (dict(out=P[8] + 4), tp.TP_ERR_UNSUPPORTED),
+    (dict(parts=[P[6], P[7] + 8]), tp.TP_ERR_UNSUPPORTED),
+    (dict(out=P[6]), tp.TP_ERR_ALIAS),
+    (dict(ob=P[7] + 128), tp.TP_ERR_ALIAS),
+    (dict(ob=P[8]), tp.TP_ERR_ALIAS),
+    (dict(res=P[8] + 256), tp.TP_ERR_ALIAS),
+])
+def test_reduce_rejects(kw, status):
+    assert reduce(**kw) == status
+    assert "tp_shard_reduce" in tp.last_error()
+
+
+def test_empty_calls_are_ok_and_touch_nothing():
+    # M == 0 is a valid empty call: TP_OK without any HIP call, so it works
+    # here with fake pointers and no GPU.
+    assert colpar(M=0) == tp.TP_OK
+    assert rowpar(M=0) == tp.TP_OK
+    assert mlp(M=0) == tp.TP_OK
+    assert reduce(M=0) == tp.TP_OK
+    assert reduce(M=0, res=P[8], flags=1, ob=P[9]) == tp.TP_OK   # in-place residual allowed
+    assert tp.last_error() == ""
+
+
+def test_binding_raises_with_status_and_message():
+    with pytest.raises(tp.TPError) as e:
+        tp.tp_colpar_gelu(P[0], P[1], P[2], P[3], 4, 64, 250, 4, 0, BF16, stream=0)
+    assert e.value.status == tp.TP_ERR_SHAPE and "divisible" in str(e.value)

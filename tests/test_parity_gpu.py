@@ -1,0 +1,266 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Every case runs the library on seeded inputs and the oracle on the same host
+arrays; the bar is a relative Frobenius error of 5e-3 for bf16 storage with
+fp32 accumulation and 1e-5 for fp32 (per checked tensor: each Y_i, Z_i and
+the reduced Z).  Full-size workloads are checked on a seeded sample of token
+rows (no step of the block mixes rows, so a row's outputs depend only on that
+row's inputs).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from megatron_tensor_transformer_colpar_amd import inputs
+from tests.harness import TOL, DeviceMLP, rel_fro, to_f64
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from megatron_tensor_transformer_colpar_amd import tp
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    print("\n[case] %s" % request.node.name, flush=True)
+    sys.stdout.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def check_all_shards(w, M, T, rows=None, seed=0, use_fused=True, shard_ids=None):
+    """Run every shard of workload w and the reduce; compare (sampled) rows."""
+    X, W1, b1, W2 = inputs.mlp_inputs(w, M=M, seed=seed)
+    dev = DeviceMLP(X, W1, b1, W2)
+    parts, Z = dev.all_shards_reduced(T, use_fused)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if rows is None else rows
+    Xr = X.f64[rows]
+    tol = TOL[w.dtype]
+    zs = []
+    for i in range(T):
+        Yr, Zr = oracle.mlp_shard(Xr, W1.f64, b1.f64, W2.f64, T, i)
+        zs.append(Zr)
+        ey = rel_fro(to_f64(parts[i][0])[rows], Yr)
+        ez = rel_fro(to_f64(parts[i][1])[rows], Zr)
+        print("  shard %d: Y_i %.2e  Z_i %.2e" % (i, ey, ez))
+        assert ey <= tol and ez <= tol, (i, ey, ez)
+    ez = rel_fro(to_f64(Z)[rows], oracle.shard_reduce(np.stack(zs)))
+    _, Zu = oracle.mlp_unsharded(Xr, W1.f64, b1.f64, W2.f64)
+    eu = rel_fro(to_f64(Z)[rows], Zu)
+    print("  reduced Z: vs sum of oracle partials %.2e, vs unsharded %.2e" % (ez, eu))
+    assert ez <= tol and eu <= tol
+    return parts, Z
+
+
+# ------------------------------------------------------------- fp32 mode
+def test_tiny_f32_two_ranks():
+    # X[8,256], W1[256,1024] split in 2, b1 = 0, W2[1024,256] split in 2.
+    check_all_shards(inputs.WORKLOADS["tiny_f32"], M=8, T=2)
+
+
+def test_tiny_f32_with_bias_and_separate_calls():
+    w = inputs.Workload(1, "tiny_f32_bias", "f32", M=8, H=256, F=1024, T=2, b_std=0.01)
+    check_all_shards(w, M=8, T=2, use_fused=False)
+
+
+def test_f32_ragged_multi_tile():
+    w = inputs.Workload(11, "f32_ragged", "f32", M=70, H=192, F=512, T=4)
+    check_all_shards(w, M=70, T=4)
+
+
+# ------------------------------------------------------- bf16 GEMM path
+def test_bf16_ragged_all_shards():
+    # M = 300 (ragged in M), shard width 320 (ragged against 128/256 tiles)
+    w = inputs.Workload(12, "bf16_ragged", "bf16", M=300, H=512, F=1280, T=4)
+    check_all_shards(w, M=300, T=4)
+
+
+def test_bf16_smallest_gemm_m():
+    # M = 33 is the first size that takes the MFMA GEMM rather than the decode path
+    w = inputs.Workload(13, "bf16_m33", "bf16", M=33, H=256, F=512, T=2)
+    check_all_shards(w, M=33, T=2, use_fused=False)
+
+
+def test_gpt_block_shard_full_size_sampled_rows():
+    # H=4096, F=16384, T=4, M=2048: all 4 shards and the reduce, as benchmarked
+    w = inputs.WORKLOADS["gpt_block_shard"]
+    check_all_shards(w, M=w.M, T=w.T, rows=inputs.row_sample(w.M, 12))
+
+
+def test_prefill_full_size_sampled_rows():
+    # H=8192, F=32768, T=8: rank 0's own weight blocks (F := F/T, T := 1), M=8192
+    w = inputs.WORKLOADS["prefill"]
+    X, W1, b1, W2 = inputs.mlp_inputs(w, shard_only=0)
+    dev = DeviceMLP(X, W1, b1, W2)
+    Y, Z = dev.shard(1, 0)
+    torch.cuda.synchronize()
+    rows = inputs.row_sample(w.M, 8)
+    Yr, Zr = oracle.mlp_shard(X.f64[rows], W1.f64, b1.f64, W2.f64, 1, 0)
+    ey, ez = rel_fro(to_f64(Y)[rows], Yr), rel_fro(to_f64(Z)[rows], Zr)
+    print("  Y_0 %.2e  Z_0 %.2e" % (ey, ez))
+    assert ey <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
+def test_full_matrix_and_rank_local_calls_agree_bitwise():
+    # Shard i of the full W1^T/W2^T (F, T, i) is the same computation as the
+    # stand-alone shard matrices (F/T, 1, 0); first and last shard.
+    w = inputs.Workload(14, "bf16_t8", "bf16", M=96, H=256, F=8 * 128, T=8)
+    X, W1, b1, W2 = inputs.mlp_inputs(w)
+    dev = DeviceMLP(X, W1, b1, W2)
+    Fs = w.F // 8
+    for i in (0, 7):
+        C = slice(i * Fs, (i + 1) * Fs)
+        loc = DeviceMLP(X, inputs.Synth("bf16", np.ascontiguousarray(W1.data[:, C])),
+                        inputs.Synth("bf16", np.ascontiguousarray(b1.data[C])),
+                        inputs.Synth("bf16", np.ascontiguousarray(W2.data[C])))
+        Yf, Zf = dev.shard(8, i)
+        Yl, Zl = loc.shard(1, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(Yf, Yl) and torch.equal(Zf, Zl)
+
+
+# ----------------------------------------------------- bf16 decode path
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32])
+@pytest.mark.parametrize("H", [192, 768, 1024])
+def test_decode_small(M, H):
+    # H picks the K split of the weight-streaming kernel (1, 2 or 8 waves)
+    w = inputs.Workload(15, "decode_small", "bf16", M=M, H=H, F=2 * 1024, T=2)
+    check_all_shards(w, M=M, T=2)
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_decode_full_size_mlp_and_outproj(M):
+    # H=8192, F/T=4096 MLP shard plus the attention out-projection shard
+    # (8 heads x 128 = 1024 context dims per rank, W_o block [1024, 8192]).
+    w = inputs.WORKLOADS["decode"]
+    X, W1, b1, W2 = inputs.mlp_inputs(w, M=M, shard_only=0)
+    dev = DeviceMLP(X, W1, b1, W2)
+    Y, Z = dev.shard(1, 0)
+    ctx, Wo = inputs.outproj_inputs(w, M=M, shard=0)
+    dctx, dWot = ctx.torch(), Wo.transposed().torch()
+    O = torch.empty(M, w.H, dtype=torch.float32, device="cuda")
+    As = w.A // w.T
+    tp.tp_rowpar_partial(dctx, dWot, O, M, w.H, As, 1, 0, tp.TP_BF16)
+    torch.cuda.synchronize()
+    Yr, Zr = oracle.mlp_shard(X.f64, W1.f64, b1.f64, W2.f64, 1, 0)
+    Or = oracle.rowpar_partial(ctx.f64, Wo.f64, 1, 0)
+    e = [rel_fro(to_f64(Y), Yr), rel_fro(to_f64(Z), Zr), rel_fro(to_f64(O), Or)]
+    print("  Y_0 %.2e  Z_0 %.2e  O_0 %.2e" % tuple(e))
+    assert max(e) <= TOL["bf16"]
+
+
+def test_outproj_head_shards_sum_to_full_projection():
+    # Head-sharded out-projection: T=8 ranks with the full W_o^T [H, A]; the
+    # reduced partials equal ctx . W_o over all heads.
+    H, A, T, M = 512, 1024, 8, 40
+    ctx = inputs.normal((M, A), 1.0, "bf16", workload=16, tensor=inputs.CTX_ID)
+    Wo = inputs.normal((A, H), 0.02, "bf16", workload=16, tensor=inputs.WO_ID)
+    dctx, dWot = ctx.torch(), Wo.transposed().torch()
+    parts = []
+    for i in range(T):
+        ci = dctx[:, i * A // T:(i + 1) * A // T].contiguous()
+        O = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        tp.tp_rowpar_partial(ci, dWot, O, M, H, A, T, i, tp.TP_BF16)
+        parts.append(O)
+    out = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    tp.tp_shard_reduce(parts, T, None, out, None, M, H)
+    torch.cuda.synchronize()
+    want = oracle.rowpar_partial(ctx.f64, Wo.f64, 1, 0)
+    assert rel_fro(to_f64(out), want) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------- reduce
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+def test_reduce_integer_partials_exact(T):
+    M, H = 37, 256
+    g = torch.Generator().manual_seed(T)
+    P = [torch.randint(-1000, 1000, (M, H), generator=g).float().cuda() for _ in range(T)]
+    R = torch.randint(-1000, 1000, (M, H), generator=g).float().cuda()
+    out = torch.empty(M, H, device="cuda")
+    tp.tp_shard_reduce(P, T, R, out, None, M, H)
+    want = oracle.shard_reduce(np.stack([to_f64(p) for p in P]), to_f64(R))
+    assert np.array_equal(to_f64(out), want)
+    # in place on the residual stream
+    tp.tp_shard_reduce(P, T, R, R, None, M, H)
+    assert np.array_equal(to_f64(R), want)
+
+
+def test_reduce_bf16_copy_is_round_to_nearest_even():
+    M, H, T = 64, 1024, 4
+    g = torch.Generator().manual_seed(5)
+    P = [torch.randn(M, H, generator=g).cuda() * 3 for _ in range(T)]
+    out = torch.empty(M, H, device="cuda")
+    ob = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    tp.tp_shard_reduce(P, T, None, out, ob, M, H)
+    host = out.cpu().numpy()
+    assert np.array_equal(ob.cpu().view(torch.int16).numpy().view(np.uint16), inputs.f32_to_bf16_bits(host))
+
+
+@pytest.mark.parametrize("H", [64, 8192])
+def test_reduce_rms_copy(H):
+    M, T = 9, 8
+    g = torch.Generator().manual_seed(H)
+    P = [torch.randn(M, H, generator=g).cuda() * 50 for _ in range(T)]
+    R = torch.randn(M, H, generator=g).cuda()
+    out = torch.empty(M, H, device="cuda")
+    ob = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    tp.tp_shard_reduce(P, T, R, out, ob, M, H, tp.TP_REDUCE_RMS_BF16)
+    want, wrms = oracle.shard_reduce(np.stack([to_f64(p) for p in P]), to_f64(R), rms_eps=tp.TP_RMS_EPS)
+    assert rel_fro(to_f64(out), want) <= 1e-6
+    assert rel_fro(to_f64(ob), wrms) <= TOL["bf16"]
+
+
+# -------------------------------------------------------- edge cases
+def test_empty_call_touches_nothing():
+    X = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros(128, 64, dtype=torch.bfloat16, device="cuda")
+    Y = torch.full((4, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    tp.tp_colpar_gelu(X, W, None, Y, 0, 64, 128, 2, 1, tp.TP_BF16)
+    torch.cuda.synchronize()
+    assert bool((Y == 7.0).all())
+
+
+@pytest.mark.parametrize("M", [8, 300])
+def test_nan_in_one_row_stays_in_that_row(M):
+    w = inputs.Workload(17, "nan_row", "bf16", M=M, H=256, F=512, T=2)
+    X, W1, b1, W2 = inputs.mlp_inputs(w)
+    X.data[3, 17] = 0x7FC0  # bf16 quiet NaN
+    dev = DeviceMLP(X, W1, b1, W2)
+    _, Z = dev.all_shards_reduced(2)
+    torch.cuda.synchronize()
+    bad = torch.isnan(Z).any(dim=1).cpu().numpy()
+    assert bad[3] and bad.sum() == 1
+
+
+@pytest.mark.parametrize("M", [8, 520])
+def test_runs_are_bitwise_deterministic(M):
+    w = inputs.Workload(18, "determinism", "bf16", M=M, H=1024, F=4096, T=4)
+    X, W1, b1, W2 = inputs.mlp_inputs(w)
+    dev = DeviceMLP(X, W1, b1, W2)
+    _, Z1 = dev.all_shards_reduced(4)
+    _, Z2 = dev.all_shards_reduced(4)
+    torch.cuda.synchronize()
+    assert torch.equal(Z1, Z2)
+
+
+def test_gelu_epilogue_accuracy_dense_grid():
+    # fp32 mode with W1 = [I | 0]: Y_i is GeLU evaluated on the exact inputs.
+    H = 64
+    x = np.linspace(-12, 12, 64 * 1024).astype(np.float32)
+    M = x.size // H
+    X = x.reshape(M, H)
+    W1 = np.eye(H, dtype=np.float32)
+    dX = torch.from_numpy(X).cuda()
+    dW1t = torch.from_numpy(np.ascontiguousarray(W1.T)).cuda()
+    Y = torch.empty(M, H, device="cuda")
+    tp.tp_colpar_gelu(dX, dW1t, None, Y, M, H, H, 1, 0, tp.TP_F32)
+    torch.cuda.synchronize()
+    want = oracle.gelu(X.astype(np.float64))
+    err = np.abs(Y.cpu().numpy().astype(np.float64) - want)
+    assert np.max(err / (1 + np.abs(want))) <= 2e-6
