@@ -9,11 +9,18 @@ for callers that want the status code itself.
 
 Importing this module raises if the library has not been built: there is no
 fallback path.
+
+torch is imported before the library is opened: torch ships its own HIP
+runtime under the same soname (libamdhip64.so.7), and the library must bind to
+that one, or the process would hold two HIP runtimes that do not share devices,
+memory or streams.
 """
 from __future__ import annotations
 
 import ctypes
 import os
+
+import torch  # noqa: F401  (loads torch's HIP runtime first; see above)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtpcolpar.so")

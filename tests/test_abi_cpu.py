@@ -150,3 +150,11 @@ def test_binding_raises_with_status_and_message():
     with pytest.raises(tp.TPError) as e:
         tp.tp_colpar_gelu(P[0], P[1], P[2], P[3], 4, 64, 250, 4, 0, BF16, stream=0)
     assert e.value.status == tp.TP_ERR_SHAPE and "divisible" in str(e.value)
+
+
+def test_one_hip_runtime_in_the_process():
+    # The binding opens the library after torch, so the library binds to the
+    # HIP runtime torch already loaded instead of loading a second one.
+    maps = open("/proc/self/maps").read()
+    libs = set(re.findall(r"\S*libamdhip64\S*", maps))
+    assert len(libs) == 1, libs
