@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of one tensor-parallel rank's share of a Megatron MLP block on MI355X.
+
+Headline step (the GPT-style block shard): bf16, H=4096, F=16384, T=4,
+M=2048 tokens; every step runs all 4 shards (column-parallel up-projection
+with fused bias + GeLU, row-parallel down-projection into an fp32 partial)
+and the on-device sum of the 4 partials.  ``value`` is that step's GEMM
+throughput in TFLOP/s (4*M*H*F flops per step; GeLU and the reduce are not
+counted), with every input resident in HBM before timing starts.
+
+Also reported on the same JSON line:
+  roofline      the dominant kernel's achieved TFLOP/s (algorithmic flops per
+                launch / mean launch time from HIP events over the timed
+                region) against the 2.5 PFLOP/s dense-bf16 MFMA peak
+  prefill       rank 0's shard at H=8192, F=32768, T=8, M=8192 (TFLOP/s)
+  decode        rank 0's MLP shard + attention out-projection shard at
+                H=8192, F/T=4096, A/T=1024, M in {1, 8, 32}, rotating over
+                weight sets larger than the last-level cache (HBM GB/s)
+  cpu_baseline  the fp64 oracle on a bounded sample of the headline rows
+  parity        the sampled rows of the last step against the oracle
+
+Only one GPU is used: ``--gpus`` above 1 is refused.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "TFLOP/s per-rank MLP shard (prefill) + HBM GB/s (decode), % of roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(name):
+    p = os.path.join(ROOT, "megatron_tensor_transformer_colpar_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from the committed counter runs, or None if the
+    kernel source changed since they were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(rec["source"]):
+        return None
+    return {"fetch_bytes": rec["fetch_bytes"], "write_bytes": rec["write_bytes"],
+            "total_bytes": rec["fetch_bytes"] + rec["write_bytes"], "scale": rec["scale"],
+            "profile": rec["profile"]}
+
+
+class Timeline:
+    """Events recorded between launches on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self, label):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.marks.append((label, e))
+
+    def durations(self):
+        """label -> list of ms, for each launch that ends at the next mark."""
+        out = {}
+        for (label, a), (_, b) in zip(self.marks, self.marks[1:]):
+            if label is not None:
+                out.setdefault(label, []).append(a.elapsed_time(b))
+        return out
+
+
+def headline(args, torch, tp, inputs):
+    w = inputs.WORKLOADS["gpt_block_shard"]
+    M, H, F, T = w.M, w.H, w.F, w.T
+    Fs = F // T
+    log("[bench] generating %s inputs (M=%d H=%d F=%d T=%d)" % (w.name, M, H, F, T))
+    X, W1, b1, W2 = inputs.mlp_inputs(w)
+    dX, dW1t, db1, dW2t = X.torch(), W1.transposed().torch(), b1.torch(), W2.transposed().torch()
+    Ys = [torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda") for _ in range(T)]
+    Zs = [torch.empty(M, H, dtype=torch.float32, device="cuda") for _ in range(T)]
+    Z = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    parts = tp.partial_array(Zs)
+    stream = torch.cuda.current_stream().cuda_stream
+    BF = tp.TP_BF16
+
+    def step(tl=None):
+        for i in range(T):
+            if tl: tl.mark("gemm_up_gelu")
+            tp.tp_colpar_gelu(dX, dW1t, db1, Ys[i], M, H, F, T, i, BF, stream)
+            if tl: tl.mark("gemm_rowpar_partial")
+            tp.tp_rowpar_partial(Ys[i], dW2t, Zs[i], M, H, F, T, i, BF, stream)
+        if tl: tl.mark("shard_reduce")
+        tp.tp_shard_reduce(parts, T, None, Z, None, M, H, 0, stream)
+
+    log("[bench] warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events between launches
+    tl = Timeline(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tl.mark(None)
+    for _ in range(args.steps):
+        step(tl)
+    tl.mark(None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = tl.marks[0][1].elapsed_time(tl.marks[-1][1])
+    ms = total_ms / args.steps
+    flops_step = 4.0 * M * H * F
+    durs = tl.durations()
+    kernels = {}
+    for name, d in durs.items():
+        mean = sum(d) / len(d)
+        entry = {"launches": len(d), "mean_us": round(mean * 1e3, 2)}
+        if name != "shard_reduce":
+            fl = 2.0 * M * H * Fs
+            entry["flops_per_launch"] = fl
+            entry["tflops"] = round(fl / (mean * 1e-3) / 1e12, 1)
+        else:
+            by = (T + 1) * M * H * 4.0
+            entry["bytes_per_launch"] = by
+            entry["gbs"] = round(by / (mean * 1e-3) / 1e9, 1)
+        kernels[name] = entry
+    log("[bench] headline: %.4f ms/step, %.1f TFLOP/s, wall %.3fs" % (ms, flops_step / (ms * 1e-3) / 1e12, wall))
+    return dict(w=w, ms=ms, flops=flops_step, kernels=kernels, X=X, W1=W1, b1=b1, W2=W2, Z=Z, wall=wall)
+
+
+def prefill(args, torch, tp):
+    # rank 0's own weight blocks (F := F/T, T := 1): H=8192, F/T=4096, M=8192
+    M, H, Fs = 8192, 8192, 4096
+    g = torch.Generator(device="cuda").manual_seed(4)
+    dX = torch.randn(M, H, generator=g, device="cuda").to(torch.bfloat16)
+    dW1t = (torch.randn(Fs, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    db1 = (torch.randn(Fs, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+    dW2t = (torch.randn(H, Fs, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(tl=None):
+        if tl: tl.mark("gemm_up_gelu")
+        tp.tp_colpar_gelu(dX, dW1t, db1, Y, M, H, Fs, 1, 0, tp.TP_BF16, stream)
+        if tl: tl.mark("gemm_rowpar_partial")
+        tp.tp_rowpar_partial(Y, dW2t, Z, M, H, Fs, 1, 0, tp.TP_BF16, stream)
+
+    for _ in range(3):
+        step()
+    tl = Timeline(torch)
+    torch.cuda.synchronize()
+    tl.mark(None)
+    n = max(3, args.steps // 5)
+    for _ in range(n):
+        step(tl)
+    tl.mark(None)
+    torch.cuda.synchronize()
+    ms = tl.marks[0][1].elapsed_time(tl.marks[-1][1]) / n
+    fl = 4.0 * M * H * Fs
+    out = {"workload": "prefill H=8192 F/T=4096 M=8192 (rank 0)", "ms_per_call": round(ms, 4),
+           "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+           "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    for name, d in tl.durations().items():
+        mean = sum(d) / len(d)
+        out[name + "_tflops"] = round(2.0 * M * H * Fs / (mean * 1e-3) / 1e12, 1)
+    log("[bench] prefill: %s" % out)
+    return out
+
+
+def decode(args, torch, tp):
+    # rank 0 at H=8192, F/T=4096, A/T=1024; R weight sets rotate so that every
+    # call streams its weights from HBM (R * 144 MiB is > 4x the 256 MB MALL).
+    H, Fs, As, R = 8192, 4096, 1024, args.decode_sets
+    g = torch.Generator(device="cuda").manual_seed(3)
+    sets = []
+    for _ in range(R):
+        sets.append(dict(
+            W1t=(torch.randn(Fs, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16),
+            b1=(torch.randn(Fs, generator=g, device="cuda") * 0.01).to(torch.bfloat16),
+            W2t=(torch.randn(H, Fs, generator=g, device="cuda") * 0.02).to(torch.bfloat16),
+            Wot=(torch.randn(H, As, generator=g, device="cuda") * 0.02).to(torch.bfloat16)))
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for M in (1, 8, 32):
+        X = torch.randn(M, H, generator=g, device="cuda").to(torch.bfloat16)
+        ctx = torch.randn(M, As, generator=g, device="cuda").to(torch.bfloat16)
+        Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+        Z = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        O = torch.empty(M, H, dtype=torch.float32, device="cuda")
+
+        def step(s, tl=None):
+            if tl: tl.mark("up")
+            tp.tp_colpar_gelu(X, s["W1t"], s["b1"], Y, M, H, Fs, 1, 0, tp.TP_BF16, stream)
+            if tl: tl.mark("down")
+            tp.tp_rowpar_partial(Y, s["W2t"], Z, M, H, Fs, 1, 0, tp.TP_BF16, stream)
+            if tl: tl.mark("outproj")
+            tp.tp_rowpar_partial(ctx, s["Wot"], O, M, H, As, 1, 0, tp.TP_BF16, stream)
+
+        for k in range(2 * R):
+            step(sets[k % R])
+        n = max(2 * R, args.steps)
+        tl = Timeline(torch)
+        torch.cuda.synchronize()
+        tl.mark(None)
+        for k in range(n):
+            step(sets[k % R], tl)
+        tl.mark(None)
+        torch.cuda.synchronize()
+        ms = tl.marks[0][1].elapsed_time(tl.marks[-1][1]) / n
+        mlp_bytes = 2.0 * (Fs * H * 2 + Fs) + M * H * 2 + M * H * 4
+        op_bytes = 2.0 * H * As + M * As * 2 + M * H * 4
+        d = {k: sum(v) / len(v) for k, v in tl.durations().items()}
+        e = {"us_per_step": round(ms * 1e3, 2),
+             "gbs": round((mlp_bytes + op_bytes) / (ms * 1e-3) / 1e9, 1),
+             "frac": round((mlp_bytes + op_bytes) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+             "up_us": round(d["up"] * 1e3, 2), "down_us": round(d["down"] * 1e3, 2),
+             "outproj_us": round(d["outproj"] * 1e3, 2),
+             "mlp_kernels_gbs": round(mlp_bytes / ((d["up"] + d["down"]) * 1e-3) / 1e9, 1)}
+        res["M=%d" % M] = e
+        log("[bench] decode M=%d: %s" % (M, e))
+    return res
+
+
+def cpu_baseline(args, hl):
+    import numpy as np
+
+    import oracle
+    from megatron_tensor_transformer_colpar_amd import inputs
+
+    w = hl["w"]
+    W1, b1, W2 = hl["W1"].f64, hl["b1"].f64, hl["W2"].f64
+    flops_row = 4.0 * w.H * w.F
+
+    def run(rows):
+        Xr = hl["X"].f64[rows]
+        t0 = time.perf_counter()
+        zs = [oracle.mlp_shard(Xr, W1, b1, W2, w.T, i)[1] for i in range(w.T)]
+        Zr = oracle.shard_reduce(np.stack(zs))
+        return time.perf_counter() - t0, Zr
+
+    probe = inputs.row_sample(w.M, 8, seed=1, include_ends=False)
+    dt, _ = run(probe)
+    n = int(min(w.M, max(8, len(probe) * args.cpu_seconds / max(dt, 1e-3))))
+    rows = inputs.row_sample(w.M, n, seed=2)
+    dt, Zr = run(rows)
+    tflops = len(rows) * flops_row / dt / 1e12
+    got = hl["Z"].double().cpu().numpy()[rows]
+    err = float(np.linalg.norm(got - Zr) / np.linalg.norm(Zr))
+    log("[bench] cpu oracle: %d rows in %.2fs (%.3f GFLOP/s), parity %.2e" % (len(rows), dt, tflops * 1e3, err))
+    cb = {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+          "sample": "%d of %d token rows of the headline step (all %d shards + reduce, fp64), %.1f s"
+                    % (len(rows), w.M, w.T, dt)}
+    par = {"rows": len(rows), "rel_fro_Z": err, "tol": 5e-3, "ok": err <= 5e-3}
+    return cb, par
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-sets", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline step only (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from megatron_tensor_transformer_colpar_amd import inputs, tp
+
+    torch.cuda.set_device(0)
+    hl = headline(args, torch, tp, inputs)
+    kernels = hl["kernels"]
+    dom = max(("gemm_up_gelu", "gemm_rowpar_partial"), key=lambda k: kernels[k]["mean_us"])
+    ach = kernels[dom]["tflops"]
+    traffic = measured_traffic(dom + "@gpt_block_shard")
+    roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": None if traffic is None else traffic["total_bytes"]}
+    if traffic is not None:
+        roof["traffic_detail"] = traffic
+    value = hl["flops"] / (hl["ms"] * 1e-3) / 1e12
+    w = hl["w"]
+    rec = {"metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(hl["ms"], 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic: seeded N(0,1) activations, N(0,0.02) weights, N(0,0.01) bias (bf16 RNE)",
+           "config": {"workload": "gpt_block_shard: all 4 TP shards + on-device reduce", "M": w.M, "H": w.H,
+                      "F": w.F, "T": w.T, "parallelism": "tp4 emulated on 1 GPU"},
+           "roofline": roof, "kernels": kernels}
+    if not args.no_extras:
+        rec["prefill"] = prefill(args, torch, tp)
+        rec["decode"] = decode(args, torch, tp)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, hl)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["gemm_bf16.hip", "gemv_bf16.hip", "gemm_f32.hip", "reduce.hip", "abi.cpp"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+COMMON = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 HIP_ONLY = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -3,25 +3,32 @@
 // with the epilogue fused: either + bias, GeLU, bf16 store (column-parallel
 // up-projection) or an fp32 store (row-parallel partial).
 //
-// Design for gfx950 (CDNA4):
-//  * v_mfma_f32_32x32x16_bf16: each wave owns a (BM/WM) x (BN/WN) block of
-//    32x32 accumulator tiles; 32x32 tiles need half the LDS fragment traffic
-//    of 16x16 tiles per flop.
-//  * K is staged through LDS in 64-wide slices (128 B per row), double
-//    buffered; global -> register loads of slice k+1 are issued before the
-//    MFMAs of slice k and written to the other LDS buffer after them, so one
-//    barrier per slice suffices.
-//  * Global loads are 16 B per lane through buffer resources rooted at the
-//    tile: rows past M or N read as zero, no clamping or branches.
-//  * LDS rows are 8 chunks of 16 B; chunk c of row r lives at slot
-//    c ^ swz(r), so the 32 rows a fragment read touches hit distinct banks.
+// Design for gfx950 (CDNA4), one 256-thread workgroup (4 waves, one per
+// SIMD) per BM x BN output tile:
+//  * v_mfma_f32_32x32x16_bf16: each wave owns a (BM/2) x (BN/2) block of
+//    32x32 accumulator tiles held in AGPRs; 32x32 tiles need half the LDS
+//    fragment traffic of 16x16 tiles per flop.
+//  * K advances in BK-wide slices (BK = 64: 128 B per row, or 32) through a
+//    ring of S LDS stages filled by direct global->LDS DMA (buffer_load ...
+//    lds, 16 B per lane): no staging registers, no ds_write, and S-1 slices
+//    in flight.
+//  * Within a slice the MFMA fragments of k-step q+1 are read from LDS while
+//    the MFMAs of k-step q run.  The barrier that publishes the next slice
+//    sits before the last k-step, so the next slice's first fragments are
+//    also read under MFMAs, and the slice just finished is refilled at once.
+//  * Each 1 KiB DMA block holds 8 rows of 8 16-byte chunks; chunk c of row r
+//    lives at slot c ^ swz(r), so fragment reads (32 rows, one chunk each)
+//    spread over all banks.  Rows past M or N read as zero through the
+//    buffer resource, so ragged tiles need no branches in the main loop.
+//  * Waits are explicit (vmcnt for the DMA of the slice about to be used,
+//    lgkmcnt(0) so no wave still reads a stage when it is refilled) followed
+//    by a bare s_barrier: a __syncthreads() fence would also drain the
+//    loads still in flight for later slices.
 #include "device_common.h"
 #include "tp_kernels.h"
 
 namespace tpk {
 namespace {
-
-constexpr int BK = 64;
 
 struct GemmDev {
     const __bf16 *A;
@@ -33,64 +40,112 @@ struct GemmDev {
     int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
-template <int BM, int BN, int WM, int WN, int EPI>
-__global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_kernel(GemmDev g)
+// LDS rows hold BK bf16 = CH chunks of 16 B; chunk c of row r sits at slot
+// c ^ swz(r).  The two swizzles make every ds_read_b128 of a fragment (32
+// consecutive rows, one chunk each) conflict-free whether the LDS serves 8
+// lanes per cycle over 32 banks or 16 lanes over 64 banks.
+template <int CH>
+__device__ __forceinline__ int swz(int row)
 {
-    constexpr int NT = WM * WN * 64;
-    constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-    constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
-    constexpr int RPI = NT / 8;                  // tile rows per load instruction
-    constexpr int A_LD = BM / RPI, B_LD = BN / RPI;
-    constexpr int STAGE = (BM + BN) * 8;         // 16-byte slots per LDS stage
-    static_assert(TM >= 1 && TN >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
-    static_assert(RPI % 16 == 0, "load rows must keep the swizzle phase");
+    if (CH == 8) return (row & 7) ^ ((row >> 3) & 1);         // 128-byte rows
+    return ((row >> 1) & 3) ^ ((row >> 3) & 1);                // 64-byte rows
+}
 
-    __shared__ u32x4 smem[2 * STAGE];
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt_hi[15:14],
+// expcnt[6:4], lgkmcnt[11:8]).
+__host__ __device__ constexpr int wait_vm_lgkm0(int vm)
+{
+    return (vm & 0xF) | (0x7 << 4) | (0x0 << 8) | ((vm >> 4) << 14);
+}
+
+template <int BM, int BN, int BK, int S>
+struct Cfg {
+    static constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile (2 x 2 waves)
+    static constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA tiles per wave
+    static constexpr int CH = BK / 8;                  // 16-byte chunks per LDS row
+    static constexpr int RB = 64 / CH;                 // rows per 1 KiB DMA block
+    static constexpr int KQ = BK / 16;                 // MFMA k-steps per slice
+    static constexpr int A_LD = BM / RB / 4, B_LD = BN / RB / 4;  // DMA instrs per wave per slice
+    static constexpr int LOADS = A_LD + B_LD;          // per thread per slice
+    static constexpr int STAGE = (BM + BN) * CH;       // 16-byte slots per stage
+    static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(S >= 2 && S <= 5, "stages");
+    static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the DMA layout");
+    static_assert((S - 2) * LOADS <= 63, "vmcnt range");
+};
+
+template <int BM, int BN, int BK, int S, bool IL, int EPI>
+__global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmDev g)
+{
+    using C_ = Cfg<BM, BN, BK, S>;
+    constexpr int TM = C_::TM, TN = C_::TN, STAGE = C_::STAGE, CH = C_::CH, RB = C_::RB, KQ = C_::KQ;
+    __shared__ u32x4 st0[STAGE];
+    __shared__ u32x4 st1[STAGE];
+    __shared__ u32x4 st2[S > 2 ? STAGE : 1];
+    __shared__ u32x4 st3[S > 3 ? STAGE : 1];
+    __shared__ u32x4 st4[S > 4 ? STAGE : 1];
 
     const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int wm = wave / WN, wn = wave % WN;
+    const int lane = t & 63;
+    // wave-uniform, kept in an SGPR so the DMA's LDS address (M0) is scalar
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
 
     int tile_m, tile_n;
     map_tile<8>(blockIdx.x, g.tiles_m, g.tiles_n, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
     const int a_rows = min(BM, g.M - m0), b_rows = min(BN, g.N - n0);
-    const __amdgpu_buffer_rsrc_t ra_src =
+    const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(g.A + (int64_t)m0 * g.lda, (uint32_t)((int64_t)a_rows * g.lda * 2));
-    const __amdgpu_buffer_rsrc_t rb_src =
+    const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(g.B + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * 2));
 
-    // loader geometry: thread t moves chunk (t & 7) of rows (t >> 3) + j*RPI
-    const int lrow = t >> 3, lkc = t & 7;
-    const int lslot = lrow * 8 + (lkc ^ swz(lrow));
-    const uint32_t a_voff = (uint32_t)(lrow * g.lda * 2 + lkc * 16);
-    const uint32_t b_voff = (uint32_t)(lrow * g.ldb * 2 + lkc * 16);
-    const uint32_t a_step = (uint32_t)(RPI * g.lda * 2), b_step = (uint32_t)(RPI * g.ldb * 2);
+    // DMA geometry: instruction j of wave w fills 1 KiB block (4j + w), i.e.
+    // rows RB(4j + w) .. +RB-1; lane L lands in slot L of the block (row
+    // L/CH, physical chunk L%CH) and so fetches logical chunk
+    // (L%CH) ^ swz(row).  The swizzle depends on row bits 0..3 only, so it
+    // is the same for every j.
+    const int drow = wave * RB + lane / CH;
+    const int dchunk = (lane % CH) ^ swz<CH>(drow);
+    const uint32_t a_voff = (uint32_t)(drow * g.lda * 2 + dchunk * 16);
+    const uint32_t b_voff = (uint32_t)(drow * g.ldb * 2 + dchunk * 16);
+    const uint32_t a_jstep = (uint32_t)(4 * RB * g.lda * 2), b_jstep = (uint32_t)(4 * RB * g.ldb * 2);
+    const int KT = g.K / BK;
 
-    u32x4 ra[A_LD], rb[B_LD];
-    auto gload = [&](int kt) {
-        const uint32_t soff = (uint32_t)kt * (BK * 2);
+    // The row offset stays in the per-lane voffset, which the buffer range
+    // check covers, so rows past M or N read zero; the in-row K offset goes
+    // in soffset.  Refills past the last slice re-read the last slice.
+    auto issue = [&](u32x4 *stage, int kt) __attribute__((always_inline)) {
+        const uint32_t koff = (uint32_t)min(kt, KT - 1) * (BK * 2);
 #pragma unroll
-        for (int j = 0; j < A_LD; ++j) ra[j] = buf_load16(ra_src, a_voff + j * a_step, soff);
+        for (int j = 0; j < C_::A_LD; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(stage + (4 * j + wave) * 64), 16,
+                                                    a_voff + j * a_jstep, koff, 0, 0);
 #pragma unroll
-        for (int j = 0; j < B_LD; ++j) rb[j] = buf_load16(rb_src, b_voff + j * b_step, soff);
-    };
-    auto sstore = [&](int buf) {
-        u32x4 *s = smem + buf * STAGE;
-#pragma unroll
-        for (int j = 0; j < A_LD; ++j) s[lslot + j * RPI * 8] = ra[j];
-#pragma unroll
-        for (int j = 0; j < B_LD; ++j) s[BM * 8 + lslot + j * RPI * 8] = rb[j];
+        for (int j = 0; j < C_::B_LD; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (4 * j + wave) * 64), 16,
+                                                    b_voff + j * b_jstep, koff, 0, 0);
     };
 
     // fragment geometry: lane reads row (lane & 31) of each 32-row tile,
-    // K chunk 2*s + (lane >> 5) of the 64-wide slice
-    const int frow = lane & 31, fhalf = lane >> 5, fsw = swz(frow);
-    const int a_base = (wm * WTM + frow) * 8;
-    const int b_base = (BM + wn * WTN + frow) * 8;
+    // K chunk 2*q + (lane >> 5) of the slice
+    const int frow = lane & 31, fhalf = lane >> 5, fsw = swz<CH>(frow);
+    const int a_base = (wm * C_::WTM + frow) * CH;
+    const int b_base = (BM + wn * C_::WTN + frow) * CH;
+
+    bf16x8 fa[2][TM], fb[2][TN];
+    auto read_frags = [&](const u32x4 *stage, int q, int p) __attribute__((always_inline)) {
+        const int slot = (2 * q + fhalf) ^ fsw;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa[p][i] = __builtin_bit_cast(bf16x8, stage[a_base + i * 32 * CH + slot]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb[p][j] = __builtin_bit_cast(bf16x8, stage[b_base + j * 32 * CH + slot]);
+    };
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -98,61 +153,116 @@ __global__ void __launch_bounds__(WM *WN * 64) gemm_bf16_kernel(GemmDev g)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    const int KT = g.K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
-        const u32x4 *s = smem + cur * STAGE;
+    auto mfmas = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int slot = (ks * 2 + fhalf) ^ fsw;
-            bf16x8 af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                af[i] = __builtin_bit_cast(bf16x8, s[a_base + i * 32 * 8 + slot]);
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                bfr[j] = __builtin_bit_cast(bf16x8, s[b_base + j * 32 * 8 + slot]);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
+    };
+
+    // Each phase issues the next k-step's fragment reads and the current
+    // k-step's MFMAs.  sched_group_barriers pin the interleave (the scheduler
+    // would otherwise sink each read down to its first use and expose the
+    // LDS latency); sched_barrier(0) closes the phase.  In the phase after
+    // the barrier the refill DMA of the finished stage is spread between the
+    // MFMAs as well, so the matrix pipe never waits for the issue of loads.
+    constexpr int NR = TM + TN, NM = TM * TN;
+    auto pin_reads = [&]() __attribute__((always_inline)) {
+        if (IL) {
+            constexpr int per = NM / NR;   // MFMAs per fragment read
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            for (int r = 0; r < NR; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
+            }
+            if (NM - per * NR > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM - per * NR, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
         }
-        if (kt + 1 < KT) sstore(cur ^ 1);
-        __syncthreads();
+    };
+    auto phase = [&](const u32x4 *stage, int q, int p_read, int p_mfma) __attribute__((always_inline)) {
+        read_frags(stage, q, p_read);
+        mfmas(p_mfma);
+        pin_reads();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto phase_refill = [&](u32x4 *refill, int kt_refill, const u32x4 *stage, int p_read,
+                            int p_mfma) __attribute__((always_inline)) {
+        read_frags(stage, 0, p_read);
+        issue(refill, kt_refill);
+        mfmas(p_mfma);
+        __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+        for (int r = 0; r < C_::LOADS; ++r) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        if (NM > C_::LOADS) __builtin_amdgcn_sched_group_barrier(0x008, NM - C_::LOADS, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One K slice held in `cur`; `nxt` holds the next slice (its DMA may
+    // still be in flight), and `cur` is refilled with slice kt + S.
+    auto slice = [&](u32x4 *cur, u32x4 *nxt, int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 1; q < KQ; ++q) phase(cur, q, q & 1, (q - 1) & 1);
+        // slice kt+1 landed (at most the S-2 younger slices still in
+        // flight) and every wave is done reading `cur`
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 2) * C_::LOADS));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        phase_refill(cur, kt + S, nxt, 0, (KQ - 1) & 1);
+    };
+
+    u32x4 *const ring[5] = {st0, st1, st2, st3, st4};
+
+    // prologue: slices 0 .. S-1 in flight, slice 0 landed and published
+#pragma unroll
+    for (int r = 0; r < S; ++r) issue(ring[r], r);
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 1) * C_::LOADS));
+    __builtin_amdgcn_s_barrier();
+    read_frags(st0, 0, 0);
+
+    int kt = 0;
+    for (; kt + S <= KT; kt += S) {
+#pragma unroll
+        for (int r = 0; r < S; ++r) slice(ring[r], ring[(r + 1) % S], kt + r);
     }
+#pragma unroll
+    for (int r = 0; r + 1 < S; ++r)
+        if (kt + r < KT) slice(ring[r], ring[r + 1], kt + r);
+    // drain the clamped refills before the workgroup exits
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
     // epilogue: accumulator element v of tile (i, j) is
     //   row 8*(v/4) + 4*(lane/32) + v%4, column lane%32
+    const bool full = (m0 + BM <= g.M) && (n0 + BN <= g.N);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * WTN + j * 32 + frow;
-        if (n >= g.N) continue;
+        const int n = n0 + wn * C_::WTN + j * 32 + frow;
+        if (!full && n >= g.N) continue;
         float b = 0.0f;
         if (EPI == EPI_BIAS_GELU && g.bias) b = (float)g.bias[n];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
+            const int mrow = m0 + wm * C_::WTM + i * 32 + 4 * fhalf;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int m = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * fhalf + (v & 3);
-                if (m >= g.M) continue;
+                const int m = mrow + 8 * (v >> 2) + (v & 3);
+                if (!full && m >= g.M) continue;
                 const float x = acc[i][j][v];
-                if (EPI == EPI_BIAS_GELU) {
+                if (EPI == EPI_BIAS_GELU)
                     static_cast<__bf16 *>(g.C)[(int64_t)m * g.ldc + n] = (__bf16)gelu_tanh(x + b);
-                } else {
+                else
                     static_cast<float *>(g.C)[(int64_t)m * g.ldc + n] = x;
-                }
             }
         }
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int BK, int S, bool IL>
 hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
 {
     GemmDev g;
@@ -168,11 +278,11 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
     g.K = (int)a.K;
     g.tiles_m = (int)((a.M + BM - 1) / BM);
     g.tiles_n = (int)((a.N + BN - 1) / BN);
-    const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(WM * WN * 64);
+    const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(256);
     if (epi == EPI_BIAS_GELU)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI_BIAS_GELU>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, IL, EPI_BIAS_GELU>), grid, block, 0, s, g);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI_STORE_F32>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, IL, EPI_STORE_F32>), grid, block, 0, s, g);
     return hipGetLastError();
 }
 
@@ -181,10 +291,22 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
 hipError_t launch_gemm_bf16(const GemmArgs &a, Epilogue epi, int num_cu, hipStream_t s)
 {
     // Largest tile that still gives every CU at least one workgroup.
-    auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
-    if (tiles(256, 256) >= num_cu) return launch_cfg<256, 256, 2, 2>(a, epi, s);
-    if (tiles(256, 128) >= num_cu) return launch_cfg<256, 128, 2, 2>(a, epi, s);
-    return launch_cfg<128, 128, 2, 2>(a, epi, s);
+    auto tiles = [&](int bm, int bn) __attribute__((always_inline)) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+#ifndef TP_GEMM_IL
+#define TP_GEMM_IL true
+#endif
+#ifndef TP_GEMM_BIG
+#define TP_GEMM_BIG 256, 256, 64, 2
+#endif
+#ifndef TP_GEMM_MID
+#define TP_GEMM_MID 256, 128, 64, 3
+#endif
+#ifndef TP_GEMM_SMALL
+#define TP_GEMM_SMALL 128, 128, 64, 3
+#endif
+    if (tiles(256, 256) >= num_cu) return launch_cfg<TP_GEMM_BIG, TP_GEMM_IL>(a, epi, s);
+    if (tiles(256, 128) >= num_cu) return launch_cfg<TP_GEMM_MID, TP_GEMM_IL>(a, epi, s);
+    return launch_cfg<TP_GEMM_SMALL, TP_GEMM_IL>(a, epi, s);
 }
 
 }  // namespace tpk
