@@ -3,8 +3,9 @@
 
 Headline step (the GPT-style block shard): bf16, H=4096, F=16384, T=4,
 M=2048 tokens; every step runs all 4 shards (column-parallel up-projection
-with fused bias + GeLU, row-parallel down-projection into an fp32 partial)
-and the on-device sum of the 4 partials.  ``value`` is that step's GEMM
+with fused bias + GeLU, then row-parallel down-projection into an fp32
+partial, each as one launch over the tiles of all 4 shards) and the
+on-device sum of the 4 partials.  ``value`` is that step's GEMM
 throughput in TFLOP/s (4*M*H*F flops per step; GeLU and the reduce are not
 counted), with every input resident in HBM before timing starts.
 
@@ -12,6 +13,7 @@ Also reported on the same JSON line:
   roofline      the dominant kernel's achieved TFLOP/s (algorithmic flops per
                 launch / mean launch time from HIP events over the timed
                 region) against the 2.5 PFLOP/s dense-bf16 MFMA peak
+  per_rank      one shard's own two launches (what one rank's GPU runs)
   prefill       rank 0's shard at H=8192, F=32768, T=8, M=8192 (TFLOP/s)
   decode        rank 0's MLP shard + attention out-projection shard at
                 H=8192, F/T=4096, A/T=1024, M in {1, 8, 32}, rotating over
@@ -92,18 +94,19 @@ def headline(args, torch, tp, inputs):
     Ys = [torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda") for _ in range(T)]
     Zs = [torch.empty(M, H, dtype=torch.float32, device="cuda") for _ in range(T)]
     Z = torch.empty(M, H, dtype=torch.float32, device="cuda")
-    parts = tp.partial_array(Zs)
+    yarr, zarr = tp.partial_array(Ys), tp.partial_array(Zs)
     stream = torch.cuda.current_stream().cuda_stream
     BF = tp.TP_BF16
 
+    # one step = the 4 ranks' column-parallel GEMMs (one launch), their
+    # row-parallel GEMMs (one launch) and the on-device sum of the partials
     def step(tl=None):
-        for i in range(T):
-            if tl: tl.mark("gemm_up_gelu")
-            tp.tp_colpar_gelu(dX, dW1t, db1, Ys[i], M, H, F, T, i, BF, stream)
-            if tl: tl.mark("gemm_rowpar_partial")
-            tp.tp_rowpar_partial(Ys[i], dW2t, Zs[i], M, H, F, T, i, BF, stream)
+        if tl: tl.mark("gemm_up_gelu")
+        tp.tp_colpar_gelu_group(dX, dW1t, db1, yarr, M, H, F, T, BF, stream)
+        if tl: tl.mark("gemm_rowpar_partial")
+        tp.tp_rowpar_partial_group(yarr, dW2t, zarr, M, H, F, T, BF, stream)
         if tl: tl.mark("shard_reduce")
-        tp.tp_shard_reduce(parts, T, None, Z, None, M, H, 0, stream)
+        tp.tp_shard_reduce(zarr, T, None, Z, None, M, H, 0, stream)
 
     log("[bench] warmup %d steps" % args.warmup)
     for _ in range(args.warmup):
@@ -123,13 +126,12 @@ def headline(args, torch, tp, inputs):
     total_ms = tl.marks[0][1].elapsed_time(tl.marks[-1][1])
     ms = total_ms / args.steps
     flops_step = 4.0 * M * H * F
-    durs = tl.durations()
     kernels = {}
-    for name, d in durs.items():
+    for name, d in tl.durations().items():
         mean = sum(d) / len(d)
         entry = {"launches": len(d), "mean_us": round(mean * 1e3, 2)}
         if name != "shard_reduce":
-            fl = 2.0 * M * H * Fs
+            fl = 2.0 * M * H * F           # all T shards in one launch
             entry["flops_per_launch"] = fl
             entry["tflops"] = round(fl / (mean * 1e-3) / 1e12, 1)
         else:
@@ -138,7 +140,32 @@ def headline(args, torch, tp, inputs):
             entry["gbs"] = round(by / (mean * 1e-3) / 1e9, 1)
         kernels[name] = entry
     log("[bench] headline: %.4f ms/step, %.1f TFLOP/s, wall %.3fs" % (ms, flops_step / (ms * 1e-3) / 1e12, wall))
-    return dict(w=w, ms=ms, flops=flops_step, kernels=kernels, X=X, W1=W1, b1=b1, W2=W2, Z=Z, wall=wall)
+
+    # one rank's own launches (what a single rank's GPU runs): shard 0 alone
+    def rank_step(tl):
+        tl.mark("up")
+        tp.tp_colpar_gelu(dX, dW1t, db1, Ys[0], M, H, F, T, 0, BF, stream)
+        tl.mark("down")
+        tp.tp_rowpar_partial(Ys[0], dW2t, Zs[0], M, H, F, T, 0, BF, stream)
+    for _ in range(3):
+        rank_step(Timeline(torch))
+    tl2 = Timeline(torch)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        rank_step(tl2)
+    tl2.mark(None)
+    torch.cuda.synchronize()
+    d2 = {k: sum(v) / len(v) for k, v in tl2.durations().items()}
+    fl = 2.0 * M * H * Fs
+    per_rank = {"workload": "shard 0 alone, M=%d H=%d F/T=%d" % (M, H, Fs),
+                "up_us": round(d2["up"] * 1e3, 2), "down_us": round(d2["down"] * 1e3, 2),
+                "up_tflops": round(fl / (d2["up"] * 1e-3) / 1e12, 1),
+                "down_tflops": round(fl / (d2["down"] * 1e-3) / 1e12, 1)}
+    # leave the full step's result in Z for the parity check
+    step()
+    torch.cuda.synchronize()
+    return dict(w=w, ms=ms, flops=flops_step, kernels=kernels, per_rank=per_rank, X=X, W1=W1, b1=b1, W2=W2,
+                Z=Z, wall=wall)
 
 
 def prefill(args, torch, tp):
@@ -306,7 +333,7 @@ def main():
            "data": "synthetic: seeded N(0,1) activations, N(0,0.02) weights, N(0,0.01) bias (bf16 RNE)",
            "config": {"workload": "gpt_block_shard: all 4 TP shards + on-device reduce", "M": w.M, "H": w.H,
                       "F": w.F, "T": w.T, "parallelism": "tp4 emulated on 1 GPU"},
-           "roofline": roof, "kernels": kernels}
+           "roofline": roof, "kernels": kernels, "per_rank": hl["per_rank"]}
     if not args.no_extras:
         rec["prefill"] = prefill(args, torch, tp)
         rec["decode"] = decode(args, torch, tp)

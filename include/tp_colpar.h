@@ -162,6 +162,32 @@ tp_status tp_mlp_shard_fwd(const void *X, const void *W1t, const void *b1, const
                            void *Y_ws, float *Z_i, int64_t M, int64_t H, int64_t F,
                            int32_t T, int32_t i, tp_dtype dt, hipStream_t stream);
 
+/*
+ * All T ranks' shares at once, for emulating the whole TP group on one GPU
+ * ([LESSON] section 1: every rank runs the same column- then row-parallel
+ * pair on its own blocks; [SLICE] summation formula: the T partials are what
+ * the All-Reduce-Sum combines).  For every i in [0, T):
+ *   tp_colpar_gelu_group:    Y_ws[i]    = GeLU(X . W1[:, C_i] + b1[C_i])   [M][Fs]
+ *   tp_rowpar_partial_group: Z_parts[i] = Y_ws[i] . W2[C_i, :]             [M][H] fp32
+ *   tp_mlp_group_fwd:        both.
+ * Bit-identical to T calls of the per-shard functions, but each projection
+ * is ONE launch over the tiles of all T shards, which fills the GPU when one
+ * shard's tiles would not.  Y_ws and Z_parts are HOST arrays of T device
+ * pointers (same dtypes and layouts as Y_i and Z_i).  Validation as the
+ * per-shard calls (with i = 0), plus: every Y_ws[j] and Z_parts[j] non-NULL
+ * (TP_ERR_NULL) and 16-byte aligned (TP_ERR_UNSUPPORTED); no shard buffer
+ * overlapping an input or another shard buffer (TP_ERR_ALIAS).
+ */
+tp_status tp_colpar_gelu_group(const void *X, const void *W1t, const void *b1, void *const *Y_ws,
+                               int64_t M, int64_t H, int64_t F, int32_t T, tp_dtype dt,
+                               hipStream_t stream);
+tp_status tp_rowpar_partial_group(const void *const *Y_ws, const void *W2t, float *const *Z_parts,
+                                  int64_t M, int64_t H, int64_t F, int32_t T, tp_dtype dt,
+                                  hipStream_t stream);
+tp_status tp_mlp_group_fwd(const void *X, const void *W1t, const void *b1, const void *W2t,
+                           void *const *Y_ws, float *const *Z_parts, int64_t M, int64_t H, int64_t F,
+                           int32_t T, tp_dtype dt, hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *tp_last_error(void);
 

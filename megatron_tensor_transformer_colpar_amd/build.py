@@ -20,6 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpcolpar.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+ROCM_INCLUDE = "/opt/rocm/include"
 ARCH = "gfx950"
 
 SOURCES = ["gemm_bf16.hip", "gemv_bf16.hip", "gemm_f32.hip", "reduce.hip", "abi.cpp"]
@@ -30,9 +32,10 @@ HIP_ONLY = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(OUT_DIR, src + ".o")
-    cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
     if src.endswith(".hip"):
-        cmd[1:1] = HIP_ONLY
+        cmd = [HIPCC, *HIP_ONLY, *COMMON, "-c", path, "-o", obj]
+    else:  # host-only C++ (the C ABI): no device code, plain g++
+        cmd = [CXX, *COMMON, "-D__HIP_PLATFORM_AMD__", "-I", ROCM_INCLUDE, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))

@@ -99,56 +99,72 @@ int num_cu()
 }
 
 // ---- launches (arguments already validated) ----
-tp_status run_colpar(const void *X, const void *W1t, const void *b1, void *Y_i, int64_t M, int64_t H,
-                     int64_t F, int32_t T, int32_t i, tp_dtype dt, hipStream_t s)
+tpk::GemmArgs empty_args()
+{
+    tpk::GemmArgs g{};
+    g.batch = 1;
+    return g;
+}
+
+hipError_t launch(const tpk::GemmArgs &g, tpk::Epilogue epi, tp_dtype dt, hipStream_t s)
+{
+    if (dt == TP_F32) return tpk::launch_gemm_f32(g, epi, s);
+    if (g.M <= 32) return tpk::launch_gemv_bf16(g, epi, num_cu(), s);
+    return tpk::launch_gemm_bf16(g, epi, num_cu(), s);
+}
+
+// Column-parallel arguments of shard i, as batch entry b.
+void colpar_entry(tpk::GemmArgs &g, int b, const void *X, const void *W1t, const void *b1, void *Y_i, int64_t H,
+                  int64_t Fs, int32_t i, int es)
+{
+    g.A[b] = X;
+    g.B[b] = static_cast<const char *>(W1t) + (int64_t)i * Fs * H * es;
+    g.bias[b] = b1 ? static_cast<const char *>(b1) + (int64_t)i * Fs * es : nullptr;
+    g.C[b] = Y_i;
+}
+
+// Row-parallel arguments of shard i (columns C_i of W2^T), as batch entry b.
+void rowpar_entry(tpk::GemmArgs &g, int b, const void *Y_i, const void *W2t, float *Z_i, int64_t Fs, int32_t i,
+                  int es)
+{
+    g.A[b] = Y_i;
+    g.B[b] = static_cast<const char *>(W2t) + (int64_t)i * Fs * es;
+    g.bias[b] = nullptr;
+    g.C[b] = Z_i;
+}
+
+tp_status run_colpar(const void *X, const void *W1t, const void *b1, void *const *Y, int nshard, int32_t i0,
+                     int64_t M, int64_t H, int64_t F, int32_t T, tp_dtype dt, hipStream_t s)
 {
     const int64_t Fs = F / T;
-    const int es = element_size(dt);
-    tpk::GemmArgs g;
-    g.A = X;
+    tpk::GemmArgs g = empty_args();
+    g.batch = nshard;
+    for (int b = 0; b < nshard; ++b) colpar_entry(g, b, X, W1t, b1, Y[b], H, Fs, i0 + b, element_size(dt));
     g.lda = H;
-    g.B = static_cast<const char *>(W1t) + (int64_t)i * Fs * H * es;
     g.ldb = H;
-    g.bias = b1 ? static_cast<const char *>(b1) + (int64_t)i * Fs * es : nullptr;
-    g.C = Y_i;
     g.ldc = Fs;
     g.M = M;
     g.N = Fs;
     g.K = H;
-    hipError_t e;
-    if (dt == TP_F32)
-        e = tpk::launch_gemm_f32(g, tpk::EPI_BIAS_GELU, s);
-    else if (M <= 32)
-        e = tpk::launch_gemv_bf16(g, tpk::EPI_BIAS_GELU, num_cu(), s);
-    else
-        e = tpk::launch_gemm_bf16(g, tpk::EPI_BIAS_GELU, num_cu(), s);
-    return e == hipSuccess ? ok() : hip_fail(e, "tp_colpar_gelu launch");
+    const hipError_t e = launch(g, tpk::EPI_BIAS_GELU, dt, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "column-parallel launch");
 }
 
-tp_status run_rowpar(const void *Y_i, const void *W2t, float *Z_i, int64_t M, int64_t H, int64_t F, int32_t T,
-                     int32_t i, tp_dtype dt, hipStream_t s)
+tp_status run_rowpar(const void *const *Y, const void *W2t, float *const *Z, int nshard, int32_t i0, int64_t M,
+                     int64_t H, int64_t F, int32_t T, tp_dtype dt, hipStream_t s)
 {
     const int64_t Fs = F / T;
-    const int es = element_size(dt);
-    tpk::GemmArgs g;
-    g.A = Y_i;
+    tpk::GemmArgs g = empty_args();
+    g.batch = nshard;
+    for (int b = 0; b < nshard; ++b) rowpar_entry(g, b, Y[b], W2t, Z[b], Fs, i0 + b, element_size(dt));
     g.lda = Fs;
-    g.B = static_cast<const char *>(W2t) + (int64_t)i * Fs * es;
     g.ldb = F;
-    g.bias = nullptr;
-    g.C = Z_i;
     g.ldc = H;
     g.M = M;
     g.N = H;
     g.K = Fs;
-    hipError_t e;
-    if (dt == TP_F32)
-        e = tpk::launch_gemm_f32(g, tpk::EPI_STORE_F32, s);
-    else if (M <= 32)
-        e = tpk::launch_gemv_bf16(g, tpk::EPI_STORE_F32, num_cu(), s);
-    else
-        e = tpk::launch_gemm_bf16(g, tpk::EPI_STORE_F32, num_cu(), s);
-    return e == hipSuccess ? ok() : hip_fail(e, "tp_rowpar_partial launch");
+    const hipError_t e = launch(g, tpk::EPI_STORE_F32, dt, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "row-parallel launch");
 }
 
 tp_status validate_colpar(const char *fn, const void *X, const void *W1t, const void *b1, const void *Y_i,
@@ -184,6 +200,45 @@ tp_status validate_rowpar(const char *fn, const void *Y_i, const void *W2t, cons
     return TP_OK;
 }
 
+// Validation of the whole-group calls.  X/W1t (column-parallel inputs) and
+// W2t (row-parallel input) may each be absent (nullptr) when the call does
+// not read them; Y_ws is an output of the column-parallel step and an input
+// of the row-parallel one; Z_parts may be absent.
+tp_status validate_group(const char *fn, const void *X, const void *W1t, const void *b1, const void *W2t,
+                         void *const *Y_ws, float *const *Z_parts, int64_t M, int64_t H, int64_t F, int32_t T,
+                         tp_dtype dt)
+{
+    tp_status st = check_shard(fn, M, H, F, T, 0, dt);
+    if (st != TP_OK) return st;
+    const bool up = X || W1t, down = W2t || Z_parts;
+    if ((up && (!X || !W1t)) || (down && (!W2t || !Z_parts)) || !Y_ws)
+        return fail(TP_ERR_NULL, "%s: a required pointer or pointer array is NULL", fn);
+    for (int j = 0; j < T; ++j)
+        if (!Y_ws[j] || (Z_parts && !Z_parts[j])) return fail(TP_ERR_NULL, "%s: shard %d's buffer is NULL", fn, j);
+    if ((st = check_dims64(fn, H, F, T)) != TP_OK) return st;
+    bool al = (!X || aligned16(X)) && (!W1t || aligned16(W1t)) && (!W2t || aligned16(W2t)) && (!b1 || aligned16(b1));
+    for (int j = 0; j < T; ++j) al = al && aligned16(Y_ws[j]) && (!Z_parts || aligned16(Z_parts[j]));
+    if (!al) return fail(TP_ERR_UNSUPPORTED, "%s: every buffer must be 16-byte aligned", fn);
+    if (M == 0) return TP_OK;
+    const int es = element_size(dt);
+    const int64_t Fs = F / T;
+    const Range none{0, 0};
+    const Range in[4] = {X ? span(X, M * H * es) : none, W1t ? span(W1t, F * H * es) : none,
+                         (b1 && up) ? span(b1, F * es) : none, W2t ? span(W2t, H * F * es) : none};
+    Range buf[2 * TP_MAX_T];
+    int nb = 0;
+    for (int j = 0; j < T; ++j) buf[nb++] = span(Y_ws[j], M * Fs * es);
+    if (Z_parts)
+        for (int j = 0; j < T; ++j) buf[nb++] = span(Z_parts[j], M * H * 4);
+    for (int a = 0; a < nb; ++a) {
+        for (const Range &r : in)
+            if (overlap(buf[a], r)) return fail(TP_ERR_ALIAS, "%s: a shard buffer overlaps an input", fn);
+        for (int b = a + 1; b < nb; ++b)
+            if (overlap(buf[a], buf[b])) return fail(TP_ERR_ALIAS, "%s: two shard buffers overlap", fn);
+    }
+    return TP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -194,7 +249,7 @@ tp_status tp_colpar_gelu(const void *X, const void *W1t, const void *b1, void *Y
     const tp_status st = validate_colpar("tp_colpar_gelu", X, W1t, b1, Y_i, M, H, F, T, i, dt);
     if (st != TP_OK) return st;
     if (M == 0) return ok();
-    return run_colpar(X, W1t, b1, Y_i, M, H, F, T, i, dt, stream);
+    return run_colpar(X, W1t, b1, &Y_i, 1, i, M, H, F, T, dt, stream);
 }
 
 tp_status tp_rowpar_partial(const void *Y_i, const void *W2t, float *Z_i, int64_t M, int64_t H, int64_t F,
@@ -203,7 +258,7 @@ tp_status tp_rowpar_partial(const void *Y_i, const void *W2t, float *Z_i, int64_
     const tp_status st = validate_rowpar("tp_rowpar_partial", Y_i, W2t, Z_i, M, H, F, T, i, dt);
     if (st != TP_OK) return st;
     if (M == 0) return ok();
-    return run_rowpar(Y_i, W2t, Z_i, M, H, F, T, i, dt, stream);
+    return run_rowpar(&Y_i, W2t, &Z_i, 1, i, M, H, F, T, dt, stream);
 }
 
 tp_status tp_mlp_shard_fwd(const void *X, const void *W1t, const void *b1, const void *W2t, void *Y_ws,
@@ -220,8 +275,39 @@ tp_status tp_mlp_shard_fwd(const void *X, const void *W1t, const void *b1, const
                   (b1 && overlap(z, span(b1, F * es))) || overlap(y, span(W2t, H * F * es))))
         return fail(TP_ERR_ALIAS, "%s: an output overlaps an input", fn);
     if (M == 0) return ok();
-    if ((st = run_colpar(X, W1t, b1, Y_ws, M, H, F, T, i, dt, stream)) != TP_OK) return st;
-    return run_rowpar(Y_ws, W2t, Z_i, M, H, F, T, i, dt, stream);
+    if ((st = run_colpar(X, W1t, b1, &Y_ws, 1, i, M, H, F, T, dt, stream)) != TP_OK) return st;
+    const void *y_in = Y_ws;
+    return run_rowpar(&y_in, W2t, &Z_i, 1, i, M, H, F, T, dt, stream);
+}
+
+tp_status tp_colpar_gelu_group(const void *X, const void *W1t, const void *b1, void *const *Y_ws, int64_t M,
+                               int64_t H, int64_t F, int32_t T, tp_dtype dt, hipStream_t stream)
+{
+    const tp_status st = validate_group("tp_colpar_gelu_group", X, W1t, b1, nullptr, Y_ws, nullptr, M, H, F, T, dt);
+    if (st != TP_OK) return st;
+    if (M == 0) return ok();
+    return run_colpar(X, W1t, b1, Y_ws, T, 0, M, H, F, T, dt, stream);
+}
+
+tp_status tp_rowpar_partial_group(const void *const *Y_ws, const void *W2t, float *const *Z_parts, int64_t M,
+                                  int64_t H, int64_t F, int32_t T, tp_dtype dt, hipStream_t stream)
+{
+    const tp_status st = validate_group("tp_rowpar_partial_group", nullptr, nullptr, nullptr, W2t,
+                                        const_cast<void *const *>(Y_ws), Z_parts, M, H, F, T, dt);
+    if (st != TP_OK) return st;
+    if (M == 0) return ok();
+    return run_rowpar(Y_ws, W2t, Z_parts, T, 0, M, H, F, T, dt, stream);
+}
+
+tp_status tp_mlp_group_fwd(const void *X, const void *W1t, const void *b1, const void *W2t, void *const *Y_ws,
+                           float *const *Z_parts, int64_t M, int64_t H, int64_t F, int32_t T, tp_dtype dt,
+                           hipStream_t stream)
+{
+    tp_status st = validate_group("tp_mlp_group_fwd", X, W1t, b1, W2t, Y_ws, Z_parts, M, H, F, T, dt);
+    if (st != TP_OK) return st;
+    if (M == 0) return ok();
+    if ((st = run_colpar(X, W1t, b1, Y_ws, T, 0, M, H, F, T, dt, stream)) != TP_OK) return st;
+    return run_rowpar(reinterpret_cast<const void *const *>(Y_ws), W2t, Z_parts, T, 0, M, H, F, T, dt, stream);
 }
 
 tp_status tp_shard_reduce(const float *const *partials, int32_t T, const float *residual, float *out_f32,

@@ -39,19 +39,24 @@ __device__ __forceinline__ float gelu_tanh(float x)
     return __fdividef(x, 1.0f + __expf(-v));
 }
 
-// Workgroup id -> (tile_m, tile_n).  Consecutive workgroup ids are dealt
-// round-robin to the 8 XCDs, each with its own L2; this remap gives every XCD
-// a contiguous run of logical tiles, and walks the logical tiles in groups of
-// GROUP_M tile-rows so the tiles in flight on one XCD share A and B panels.
+// Workgroup id -> (batch entry, tile_m, tile_n).  Consecutive workgroup ids
+// are dealt round-robin to the 8 XCDs, each with its own L2; this remap gives
+// every XCD a contiguous run of logical tiles, and walks the logical tiles of
+// one batch entry in groups of GROUP_M tile-rows so the tiles in flight on
+// one XCD share A and B panels.
 template <int GROUP_M>
-__device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+__device__ __forceinline__ void map_tile(int bid, int batch, int tiles_m, int tiles_n, int &bt, int &tm,
+                                         int &tn)
 {
-    const int total = tiles_m * tiles_n;
+    const int per_batch = tiles_m * tiles_n;
+    const int total = batch * per_batch;
     int logical = bid;
     if ((total & 7) == 0) {
         const int per_xcd = total >> 3;
         logical = (bid & 7) * per_xcd + (bid >> 3);
     }
+    bt = logical / per_batch;
+    logical -= bt * per_batch;
     const int per_group = GROUP_M * tiles_n;
     const int group = logical / per_group;
     const int first_m = group * GROUP_M;

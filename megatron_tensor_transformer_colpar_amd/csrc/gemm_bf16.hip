@@ -31,13 +31,13 @@ namespace tpk {
 namespace {
 
 struct GemmDev {
-    const __bf16 *A;
-    const __bf16 *B;
-    const __bf16 *bias;
-    void *C;
+    const __bf16 *A[kMaxBatch];
+    const __bf16 *B[kMaxBatch];
+    const __bf16 *bias[kMaxBatch];
+    void *C[kMaxBatch];
     int64_t lda, ldb, ldc;
     int M, N, K;
-    int tiles_m, tiles_n;
+    int tiles_m, tiles_n, batch;
 };
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
@@ -93,15 +93,19 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmDev g)
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    int tile_m, tile_n;
-    map_tile<8>(blockIdx.x, g.tiles_m, g.tiles_n, tile_m, tile_n);
+    int bt, tile_m, tile_n;
+    map_tile<8>(blockIdx.x, g.batch, g.tiles_m, g.tiles_n, bt, tile_m, tile_n);
     const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const __bf16 *const Abase = g.A[bt];
+    const __bf16 *const Bbase = g.B[bt];
+    const __bf16 *const bias_p = g.bias[bt];
+    void *const Cbase = g.C[bt];
 
     const int a_rows = min(BM, g.M - m0), b_rows = min(BN, g.N - n0);
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(g.A + (int64_t)m0 * g.lda, (uint32_t)((int64_t)a_rows * g.lda * 2));
+        make_rsrc(Abase + (int64_t)m0 * g.lda, (uint32_t)((int64_t)a_rows * g.lda * 2));
     const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(g.B + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * 2));
+        make_rsrc(Bbase + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * 2));
 
     // DMA geometry: instruction j of wave w fills 1 KiB block (4j + w), i.e.
     // rows RB(4j + w) .. +RB-1; lane L lands in slot L of the block (row
@@ -153,12 +157,15 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmDev g)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
+    // B is the MFMA's first operand, so the 32x32 result is the tile
+    // transposed: lane l ends up with 4 consecutive columns of row l%32,
+    // which the epilogue stores as one vector.
     auto mfmas = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[p][i], fb[p][j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[p][j], fa[p][i], acc[i][j], 0, 0, 0);
     };
 
     // Each phase issues the next k-step's fragment reads and the current
@@ -236,27 +243,40 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmDev g)
     // drain the clamped refills before the workgroup exits
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
-    // epilogue: accumulator element v of tile (i, j) is
-    //   row 8*(v/4) + 4*(lane/32) + v%4, column lane%32
+    // epilogue: element v of accumulator (i, j) is C[m][n] with
+    //   m = tile row base + lane%32,  n = tile column base + 8*(v/4) + 4*(lane/32) + v%4,
+    // so each lane owns runs of 4 consecutive columns: one 16-byte fp32
+    // store or one 8-byte bf16 store per run.
     const bool full = (m0 + BM <= g.M) && (n0 + BN <= g.N);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * C_::WTN + j * 32 + frow;
-        if (!full && n >= g.N) continue;
-        float b = 0.0f;
-        if (EPI == EPI_BIAS_GELU && g.bias) b = (float)g.bias[n];
+        const int nb = n0 + wn * C_::WTN + j * 32 + 4 * fhalf;
+        f32x4 bias[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bias[q] = f32x4{};
+            if (EPI == EPI_BIAS_GELU && bias_p && (full || nb + 8 * q < g.N)) {
+                const bf16x4 b4 = *reinterpret_cast<const bf16x4 *>(bias_p + nb + 8 * q);
+                bias[q] = f32x4{(float)b4[0], (float)b4[1], (float)b4[2], (float)b4[3]};
+            }
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int mrow = m0 + wm * C_::WTM + i * 32 + 4 * fhalf;
+            const int m = m0 + wm * C_::WTM + i * 32 + frow;
+            if (!full && m >= g.M) continue;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = mrow + 8 * (v >> 2) + (v & 3);
-                if (!full && m >= g.M) continue;
-                const float x = acc[i][j][v];
-                if (EPI == EPI_BIAS_GELU)
-                    static_cast<__bf16 *>(g.C)[(int64_t)m * g.ldc + n] = (__bf16)gelu_tanh(x + b);
-                else
-                    static_cast<float *>(g.C)[(int64_t)m * g.ldc + n] = x;
+            for (int q = 0; q < 4; ++q) {
+                const int n = nb + 8 * q;
+                if (!full && n >= g.N) continue;
+                f32x4 x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if (EPI == EPI_BIAS_GELU) {
+                    x += bias[q];
+                    const bf16x4 y = {(__bf16)gelu_tanh(x[0]), (__bf16)gelu_tanh(x[1]), (__bf16)gelu_tanh(x[2]),
+                                      (__bf16)gelu_tanh(x[3])};
+                    *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * g.ldc + n) = y;
+                } else {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * g.ldc + n) = x;
+                }
             }
         }
     }
@@ -266,19 +286,23 @@ template <int BM, int BN, int BK, int S, bool IL>
 hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
 {
     GemmDev g;
-    g.A = static_cast<const __bf16 *>(a.A);
-    g.B = static_cast<const __bf16 *>(a.B);
-    g.bias = static_cast<const __bf16 *>(a.bias);
-    g.C = a.C;
+    for (int b = 0; b < kMaxBatch; ++b) {
+        const int src = b < a.batch ? b : 0;
+        g.A[b] = static_cast<const __bf16 *>(a.A[src]);
+        g.B[b] = static_cast<const __bf16 *>(a.B[src]);
+        g.bias[b] = static_cast<const __bf16 *>(a.bias[src]);
+        g.C[b] = a.C[src];
+    }
     g.lda = a.lda;
     g.ldb = a.ldb;
     g.ldc = a.ldc;
     g.M = (int)a.M;
     g.N = (int)a.N;
     g.K = (int)a.K;
+    g.batch = a.batch;
     g.tiles_m = (int)((a.M + BM - 1) / BM);
     g.tiles_n = (int)((a.N + BN - 1) / BN);
-    const dim3 grid((unsigned)(g.tiles_m * g.tiles_n)), block(256);
+    const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(256);
     if (epi == EPI_BIAS_GELU)
         hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, IL, EPI_BIAS_GELU>), grid, block, 0, s, g);
     else

@@ -84,24 +84,28 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmF32Dev g)
 
 hipError_t launch_gemm_f32(const GemmArgs &a, Epilogue epi, hipStream_t s)
 {
-    GemmF32Dev g;
-    g.A = static_cast<const float *>(a.A);
-    g.B = static_cast<const float *>(a.B);
-    g.bias = static_cast<const float *>(a.bias);
-    g.C = static_cast<float *>(a.C);
-    g.lda = a.lda;
-    g.ldb = a.ldb;
-    g.ldc = a.ldc;
-    g.M = (int)a.M;
-    g.N = (int)a.N;
-    g.K = (int)a.K;
-    g.tiles_n = (int)((a.N + TB - 1) / TB);
-    const dim3 grid((unsigned)(g.tiles_n * ((a.M + TB - 1) / TB)));
-    if (epi == EPI_BIAS_GELU)
-        hipLaunchKernelGGL(gemm_f32_kernel<EPI_BIAS_GELU>, grid, dim3(256), 0, s, g);
-    else
-        hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE_F32>, grid, dim3(256), 0, s, g);
-    return hipGetLastError();
+    for (int b = 0; b < a.batch; ++b) {
+        GemmF32Dev g;
+        g.A = static_cast<const float *>(a.A[b]);
+        g.B = static_cast<const float *>(a.B[b]);
+        g.bias = static_cast<const float *>(a.bias[b]);
+        g.C = static_cast<float *>(a.C[b]);
+        g.lda = a.lda;
+        g.ldb = a.ldb;
+        g.ldc = a.ldc;
+        g.M = (int)a.M;
+        g.N = (int)a.N;
+        g.K = (int)a.K;
+        g.tiles_n = (int)((a.N + TB - 1) / TB);
+        const dim3 grid((unsigned)(g.tiles_n * ((a.M + TB - 1) / TB)));
+        if (epi == EPI_BIAS_GELU)
+            hipLaunchKernelGGL(gemm_f32_kernel<EPI_BIAS_GELU>, grid, dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE_F32>, grid, dim3(256), 0, s, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace tpk

@@ -21,10 +21,10 @@ namespace {
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
 struct GemvDev {
-    const __bf16 *X;
-    const __bf16 *W;
-    const __bf16 *bias;
-    void *C;
+    const __bf16 *X[kMaxBatch];
+    const __bf16 *W[kMaxBatch];
+    const __bf16 *bias[kMaxBatch];
+    void *C[kMaxBatch];
     int64_t ldx, ldw, ldc;
     int M, N, K;
 };
@@ -36,12 +36,15 @@ __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int n0 = blockIdx.x * 16;
+    const int bt = blockIdx.y;   // batch entry (TP shard)
+    const __bf16 *const Xb = g.X[bt];
+    const __bf16 *const Wb = g.W[bt];
     const int Kw = g.K / KS;
     const int kbeg = w * Kw;
 
     const __amdgpu_buffer_rsrc_t wsrc =
-        make_rsrc(g.W + (int64_t)n0 * g.ldw, (uint32_t)(16 * g.ldw * 2));
-    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(g.X, (uint32_t)((int64_t)g.M * g.ldx * 2));
+        make_rsrc(Wb + (int64_t)n0 * g.ldw, (uint32_t)(16 * g.ldw * 2));
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(Xb, (uint32_t)((int64_t)g.M * g.ldx * 2));
 
     // lane geometry of the 16x16x32 MFMA operands: row (lane & 15), K chunk
     // (lane >> 4) of 8 elements
@@ -90,18 +93,18 @@ __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
         const int n = n0 + 4 * (l >> 4) + v;
         if (m >= g.M) continue;
         if (EPI == EPI_BIAS_GELU) {
-            const float b = g.bias ? (float)g.bias[n] : 0.0f;
-            static_cast<__bf16 *>(g.C)[(int64_t)m * g.ldc + n] = (__bf16)gelu_tanh(s + b);
+            const float b = g.bias[bt] ? (float)g.bias[bt][n] : 0.0f;
+            static_cast<__bf16 *>(g.C[bt])[(int64_t)m * g.ldc + n] = (__bf16)gelu_tanh(s + b);
         } else {
-            static_cast<float *>(g.C)[(int64_t)m * g.ldc + n] = s;
+            static_cast<float *>(g.C[bt])[(int64_t)m * g.ldc + n] = s;
         }
     }
 }
 
 template <int EPI, int MT>
-hipError_t launch_mt(const GemvDev &g, hipStream_t s)
+hipError_t launch_mt(const GemvDev &g, int batch, hipStream_t s)
 {
-    const dim3 grid((unsigned)(g.N / 16));
+    const dim3 grid((unsigned)(g.N / 16), (unsigned)batch);
     // Split K over as many waves as keeps >= 128 elements per wave and a
     // 128-element (U = 4) or 64-element (U = 2) inner step.
     if (g.K % (8 * 128) == 0)
@@ -120,10 +123,13 @@ hipError_t launch_mt(const GemvDev &g, hipStream_t s)
 hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int /*num_cu*/, hipStream_t s)
 {
     GemvDev g;
-    g.X = static_cast<const __bf16 *>(a.A);
-    g.W = static_cast<const __bf16 *>(a.B);
-    g.bias = static_cast<const __bf16 *>(a.bias);
-    g.C = a.C;
+    for (int b = 0; b < kMaxBatch; ++b) {
+        const int src = b < a.batch ? b : 0;
+        g.X[b] = static_cast<const __bf16 *>(a.A[src]);
+        g.W[b] = static_cast<const __bf16 *>(a.B[src]);
+        g.bias[b] = static_cast<const __bf16 *>(a.bias[src]);
+        g.C[b] = a.C[src];
+    }
     g.ldx = a.lda;
     g.ldw = a.ldb;
     g.ldc = a.ldc;
@@ -132,8 +138,8 @@ hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int /*num_cu*/, hip
     g.K = (int)a.K;
     const bool two = a.M > 16;
     if (epi == EPI_BIAS_GELU)
-        return two ? launch_mt<EPI_BIAS_GELU, 2>(g, s) : launch_mt<EPI_BIAS_GELU, 1>(g, s);
-    return two ? launch_mt<EPI_STORE_F32, 2>(g, s) : launch_mt<EPI_STORE_F32, 1>(g, s);
+        return two ? launch_mt<EPI_BIAS_GELU, 2>(g, a.batch, s) : launch_mt<EPI_BIAS_GELU, 1>(g, a.batch, s);
+    return two ? launch_mt<EPI_STORE_F32, 2>(g, a.batch, s) : launch_mt<EPI_STORE_F32, 1>(g, a.batch, s);
 }
 
 }  // namespace tpk

@@ -3,7 +3,7 @@
 // range, K a multiple of 64, N a multiple of 64, 16-byte aligned pointers.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace tpk {
@@ -16,15 +16,20 @@ enum Epilogue : int {
 
 // C[m][n] = sum_k A[m][k] * B[n][k]  (both operands K-contiguous), then the
 // epilogue.  A: M rows, stride lda; B: N rows, stride ldb; C: stride ldc.
+// `batch` independent problems of the same shape (one per TP shard when the
+// whole TP group is emulated on one GPU) may be launched together; entry b
+// of each pointer array belongs to problem b.
+constexpr int kMaxBatch = 8;
 struct GemmArgs {
-    const void *A;
+    const void *A[kMaxBatch];
     int64_t lda;
-    const void *B;
+    const void *B[kMaxBatch];
     int64_t ldb;
-    const void *bias;  // [N] or nullptr (EPI_BIAS_GELU only)
-    void *C;
+    const void *bias[kMaxBatch];  // [N] or nullptr (EPI_BIAS_GELU only)
+    void *C[kMaxBatch];
     int64_t ldc;
     int64_t M, N, K;
+    int batch;
 };
 
 // bf16 x bf16 -> fp32 accumulate, MFMA tiles; for M > 32.

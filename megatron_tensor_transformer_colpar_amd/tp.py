@@ -45,7 +45,12 @@ raw.tp_colpar_gelu.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
 raw.tp_rowpar_partial.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
 raw.tp_shard_reduce.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _i64, _i64, _u32, _vp]
 raw.tp_mlp_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
-for _f in (raw.tp_colpar_gelu, raw.tp_rowpar_partial, raw.tp_shard_reduce, raw.tp_mlp_shard_fwd):
+_pp = ctypes.POINTER(_vp)
+raw.tp_colpar_gelu_group.argtypes = [_vp, _vp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
+raw.tp_rowpar_partial_group.argtypes = [_pp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
+raw.tp_mlp_group_fwd.argtypes = [_vp, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
+for _f in (raw.tp_colpar_gelu, raw.tp_rowpar_partial, raw.tp_shard_reduce, raw.tp_mlp_shard_fwd,
+           raw.tp_colpar_gelu_group, raw.tp_rowpar_partial_group, raw.tp_mlp_group_fwd):
     _f.restype = ctypes.c_int
 raw.tp_last_error.argtypes = []
 raw.tp_last_error.restype = ctypes.c_char_p
@@ -53,7 +58,8 @@ raw.tp_version.argtypes = []
 raw.tp_version.restype = ctypes.c_char_p
 
 EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_shard_fwd",
-           "tp_last_error", "tp_version")
+           "tp_colpar_gelu_group", "tp_rowpar_partial_group", "tp_mlp_group_fwd", "tp_last_error",
+           "tp_version")
 
 
 class TPError(RuntimeError):
@@ -102,7 +108,7 @@ def tp_rowpar_partial(Y_i, W2t, Z_i, M, H, F, T, i, dt=TP_BF16, stream=None):
 
 
 def partial_array(partials):
-    """Host array of device pointers for tp_shard_reduce."""
+    """Host array of device pointers (tp_shard_reduce, tp_mlp_group_fwd)."""
     return (_vp * len(partials))(*[_ptr(p) for p in partials])
 
 
@@ -115,3 +121,20 @@ def tp_shard_reduce(partials, T, residual, out_f32, out_bf16, M, H, flags=0, str
 def tp_mlp_shard_fwd(X, W1t, b1, W2t, Y_ws, Z_i, M, H, F, T, i, dt=TP_BF16, stream=None):
     _check(raw.tp_mlp_shard_fwd(_ptr(X), _ptr(W1t), _ptr(b1), _ptr(W2t), _ptr(Y_ws), _ptr(Z_i), M, H, F,
                                 T, i, dt, _stream(stream)))
+
+
+def _arr(xs):
+    return xs if isinstance(xs, ctypes.Array) else partial_array(xs)
+
+
+def tp_colpar_gelu_group(X, W1t, b1, Y_ws, M, H, F, T, dt=TP_BF16, stream=None):
+    _check(raw.tp_colpar_gelu_group(_ptr(X), _ptr(W1t), _ptr(b1), _arr(Y_ws), M, H, F, T, dt, _stream(stream)))
+
+
+def tp_rowpar_partial_group(Y_ws, W2t, Z_parts, M, H, F, T, dt=TP_BF16, stream=None):
+    _check(raw.tp_rowpar_partial_group(_arr(Y_ws), _ptr(W2t), _arr(Z_parts), M, H, F, T, dt, _stream(stream)))
+
+
+def tp_mlp_group_fwd(X, W1t, b1, W2t, Y_ws, Z_parts, M, H, F, T, dt=TP_BF16, stream=None):
+    _check(raw.tp_mlp_group_fwd(_ptr(X), _ptr(W1t), _ptr(b1), _ptr(W2t), _arr(Y_ws), _arr(Z_parts), M, H, F, T,
+                                dt, _stream(stream)))

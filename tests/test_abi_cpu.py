@@ -158,3 +158,39 @@ def test_one_hip_runtime_in_the_process():
     maps = open("/proc/self/maps").read()
     libs = set(re.findall(r"\S*libamdhip64\S*", maps))
     assert len(libs) == 1, libs
+
+
+def arr(*ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def group(X=P[0], W1=P[1], b=P[2], W2=P[4], Y=None, Z=None, M=4, H=64, F=256, T=2, dt=BF16):
+    Y = arr(P[6], P[7]) if Y is None else Y
+    Z = arr(P[8], P[9]) if Z is None else Z
+    return tp.raw.tp_mlp_group_fwd(X, W1, b, W2, Y, Z, M, H, F, T, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=3), tp.TP_ERR_SHAPE),
+    (dict(X=None), tp.TP_ERR_NULL),
+    (dict(W2=None), tp.TP_ERR_NULL),
+    (dict(Y=arr(P[6], None)), tp.TP_ERR_NULL),
+    (dict(Z=arr(None, P[9])), tp.TP_ERR_NULL),
+    (dict(Y=arr(P[6], P[7] + 4)), tp.TP_ERR_UNSUPPORTED),
+    (dict(Y=arr(P[6], P[6] + 256)), tp.TP_ERR_ALIAS),     # two shards' Y overlap
+    (dict(Z=arr(P[8], P[6])), tp.TP_ERR_ALIAS),           # Z over a Y
+    (dict(Z=arr(P[0], P[9])), tp.TP_ERR_ALIAS),           # Z over X
+    (dict(Y=arr(P[4] + 64, P[7])), tp.TP_ERR_ALIAS),      # Y over W2t
+])
+def test_group_rejects(kw, status):
+    assert group(**kw) == status
+    assert "tp_mlp_group_fwd" in tp.last_error()
+
+
+def test_group_halves_reject_and_accept_empty():
+    Y, Z = arr(P[6], P[7]), arr(P[8], P[9])
+    assert tp.raw.tp_colpar_gelu_group(P[0], None, None, Y, 4, 64, 256, 2, BF16, None) == tp.TP_ERR_NULL
+    assert tp.raw.tp_rowpar_partial_group(Y, P[4], None, 4, 64, 256, 2, BF16, None) == tp.TP_ERR_NULL
+    assert tp.raw.tp_colpar_gelu_group(P[0], P[1], P[2], Y, 0, 64, 256, 2, BF16, None) == tp.TP_OK
+    assert tp.raw.tp_rowpar_partial_group(Y, P[4], Z, 0, 64, 256, 2, BF16, None) == tp.TP_OK
+    assert group(M=0) == tp.TP_OK

@@ -175,6 +175,60 @@ def test_outproj_head_shards_sum_to_full_projection():
     assert rel_fro(to_f64(out), want) <= TOL["bf16"]
 
 
+# ------------------------------------------- whole-group (all shards) calls
+def group_outputs(dev, T, split=False):
+    Fs = dev.F // T
+    tdt = torch.bfloat16 if dev.dt == "bf16" else torch.float32
+    Ys = [torch.empty(dev.M, Fs, dtype=tdt, device="cuda") for _ in range(T)]
+    Zs = [torch.empty(dev.M, dev.H, dtype=torch.float32, device="cuda") for _ in range(T)]
+    dt = tp.TP_BF16 if dev.dt == "bf16" else tp.TP_F32
+    if split:
+        tp.tp_colpar_gelu_group(dev.X, dev.W1t, dev.b1, Ys, dev.M, dev.H, dev.F, T, dt)
+        tp.tp_rowpar_partial_group(Ys, dev.W2t, Zs, dev.M, dev.H, dev.F, T, dt)
+    else:
+        tp.tp_mlp_group_fwd(dev.X, dev.W1t, dev.b1, dev.W2t, Ys, Zs, dev.M, dev.H, dev.F, T, dt)
+    return Ys, Zs
+
+
+@pytest.mark.parametrize("dt,M,H,F,T,split", [
+    ("bf16", 300, 512, 1280, 4, False),    # MFMA GEMM, ragged M and N
+    ("bf16", 2048, 1024, 4096, 4, True),   # enough tiles for the 256x256 config
+    ("bf16", 8, 1024, 4096, 8, False),     # decode kernel, all 8 shards batched
+    ("bf16", 32, 512, 2048, 2, True),
+    ("f32", 40, 256, 1024, 2, False),
+])
+def test_group_matches_per_shard_calls_bitwise(dt, M, H, F, T, split):
+    w = inputs.Workload(19, "group", dt, M=M, H=H, F=F, T=T)
+    X, W1, b1, W2 = inputs.mlp_inputs(w)
+    dev = DeviceMLP(X, W1, b1, W2)
+    Ys, Zs = group_outputs(dev, T, split)
+    per = [dev.shard(T, i) for i in range(T)]
+    torch.cuda.synchronize()
+    for i in range(T):
+        assert torch.equal(Ys[i], per[i][0]) and torch.equal(Zs[i], per[i][1]), i
+    rows = inputs.row_sample(M, 6)
+    for i in (0, T - 1):
+        Yr, Zr = oracle.mlp_shard(X.f64[rows], W1.f64, b1.f64, W2.f64, T, i)
+        assert rel_fro(to_f64(Ys[i])[rows], Yr) <= TOL[dt] and rel_fro(to_f64(Zs[i])[rows], Zr) <= TOL[dt]
+
+
+def test_group_gpt_block_shard_full_size():
+    # the benchmarked launch: H=4096, F=16384, T=4, M=2048, all shards in one
+    # launch per projection, then the reduce; sampled rows against the oracle
+    w = inputs.WORKLOADS["gpt_block_shard"]
+    X, W1, b1, W2 = inputs.mlp_inputs(w)
+    dev = DeviceMLP(X, W1, b1, W2)
+    Ys, Zs = group_outputs(dev, w.T)
+    Z = torch.empty(w.M, w.H, dtype=torch.float32, device="cuda")
+    tp.tp_shard_reduce(Zs, w.T, None, Z, None, w.M, w.H)
+    torch.cuda.synchronize()
+    rows = inputs.row_sample(w.M, 10, seed=5)
+    _, Zu = oracle.mlp_unsharded(X.f64[rows], W1.f64, b1.f64, W2.f64)
+    e = rel_fro(to_f64(Z)[rows], Zu)
+    print("  reduced Z vs unsharded oracle: %.2e" % e)
+    assert e <= TOL["bf16"]
+
+
 # ------------------------------------------------------------- reduce
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
 def test_reduce_integer_partials_exact(T):
