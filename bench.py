@@ -304,6 +304,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline step only (for profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
@@ -315,6 +317,14 @@ def main():
     from megatron_tensor_transformer_colpar_amd import inputs, tp
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     hl = headline(args, torch, tp, inputs)
     kernels = hl["kernels"]
     dom = max(("gemm_up_gelu", "gemm_rowpar_partial"), key=lambda k: kernels[k]["mean_us"])

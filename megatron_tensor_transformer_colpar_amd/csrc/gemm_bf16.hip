@@ -315,7 +315,9 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
 hipError_t launch_gemm_bf16(const GemmArgs &a, Epilogue epi, int num_cu, hipStream_t s)
 {
     // Largest tile that still gives every CU at least one workgroup.
-    auto tiles = [&](int bm, int bn) __attribute__((always_inline)) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+    auto tiles = [&](int bm, int bn) __attribute__((always_inline)) {
+        return a.batch * ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+    };
 #ifndef TP_GEMM_IL
 #define TP_GEMM_IL true
 #endif
