@@ -188,6 +188,32 @@ tp_status tp_mlp_group_fwd(const void *X, const void *W1t, const void *b1, const
                            void *const *Y_ws, float *const *Z_parts, int64_t M, int64_t H, int64_t F,
                            int32_t T, tp_dtype dt, hipStream_t stream);
 
+/*
+ * One block of a layer stack, with the whole TP group emulated on one GPU
+ * (bf16 storage, fp32 residual stream).  The two all-reduces of a layer
+ * follow the attention output projection and the MLP and sit on the
+ * residual paths ([SLICE] "All-Reduce Synchronization"; [GUIDE] "Walking
+ * through a transformer block"):
+ *   parts[i] = ctx[i] . W_o[A_i, :]                 (head-sharded out-proj)
+ *   h       += parts[0] + ... + parts[T-1]
+ *   xhat     = bf16(h / sqrt(mean_row(h^2) + TP_RMS_EPS))   (not from the
+ *              pages: keeps a deep stack with no normalisation layer finite)
+ *   Y_ws[i]  = GeLU(xhat . W1[:, C_i] + b1[C_i]),  parts[i] = Y_ws[i] . W2[C_i, :]
+ *   h       += parts[0] + ... + parts[T-1]
+ *   h      [M][H] fp32, read and written (the residual stream)
+ *   xhat   [M][H] bf16 workspace (written)
+ *   ctx    HOST array of T device pointers, each [M][A/T] bf16 (rank i's heads)
+ *   Wot    W_o^T [H][A] bf16;  W1t, b1, W2t as tp_mlp_group_fwd
+ *   Y_ws, parts  HOST arrays of T workspaces ([M][F/T] bf16, [M][H] fp32)
+ * Validation: as tp_mlp_group_fwd for the MLP and for the out-projection
+ * (with F := A), plus h, xhat non-NULL and 16-byte aligned and disjoint from
+ * every other buffer.
+ */
+tp_status tp_layer_fwd(float *h, void *xhat, const void *const *ctx, const void *Wot, int64_t A,
+                       const void *W1t, const void *b1, const void *W2t, void *const *Y_ws,
+                       float *const *parts, int64_t M, int64_t H, int64_t F, int32_t T,
+                       hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *tp_last_error(void);
 

@@ -310,6 +310,46 @@ tp_status tp_mlp_group_fwd(const void *X, const void *W1t, const void *b1, const
     return run_rowpar(reinterpret_cast<const void *const *>(Y_ws), W2t, Z_parts, T, 0, M, H, F, T, dt, stream);
 }
 
+tp_status tp_layer_fwd(float *h, void *xhat, const void *const *ctx, const void *Wot, int64_t A, const void *W1t,
+                       const void *b1, const void *W2t, void *const *Y_ws, float *const *parts, int64_t M, int64_t H,
+                       int64_t F, int32_t T, hipStream_t stream)
+{
+    const char *fn = "tp_layer_fwd";
+    if (!h || !xhat || !ctx) return fail(TP_ERR_NULL, "%s: h, xhat and ctx must be non-NULL", fn);
+    tp_status st = validate_group(fn, nullptr, nullptr, nullptr, Wot, const_cast<void *const *>(ctx), parts, M, H,
+                                  A, T, TP_BF16);
+    if (st != TP_OK) return st;
+    if ((st = validate_group(fn, xhat, W1t, b1, W2t, Y_ws, parts, M, H, F, T, TP_BF16)) != TP_OK) return st;
+    if (!aligned16(h) || !aligned16(xhat)) return fail(TP_ERR_UNSUPPORTED, "%s: h and xhat must be 16-byte aligned", fn);
+    if (M > 0) {
+        const Range rh = span(h, M * H * 4), rx = span(xhat, M * H * 2);
+        const Range others[4] = {span(Wot, H * A * 2), span(W1t, F * H * 2), b1 ? span(b1, F * 2) : Range{0, 0},
+                                 span(W2t, H * F * 2)};
+        if (overlap(rh, rx)) return fail(TP_ERR_ALIAS, "%s: h and xhat overlap", fn);
+        for (const Range &r : others)
+            if (overlap(rh, r) || overlap(rx, r)) return fail(TP_ERR_ALIAS, "%s: h or xhat overlaps a weight", fn);
+        for (int j = 0; j < T; ++j) {
+            const Range bufs[3] = {span(ctx[j], M * (A / T) * 2), span(Y_ws[j], M * (F / T) * 2),
+                                   span(parts[j], M * H * 4)};
+            for (const Range &b : bufs)
+                if (overlap(rh, b) || overlap(rx, b))
+                    return fail(TP_ERR_ALIAS, "%s: h or xhat overlaps shard %d's buffers", fn, j);
+        }
+    }
+    if (M == 0) return ok();
+    // attention output projection of every rank, then h += sum, xhat = rms copy
+    if ((st = run_rowpar(ctx, Wot, parts, T, 0, M, H, A, T, TP_BF16, stream)) != TP_OK) return st;
+    hipError_t e = tpk::launch_shard_reduce(parts, T, h, h, xhat, M, H, true, TP_RMS_EPS, stream);
+    if (e != hipSuccess) return hip_fail(e, "tp_layer_fwd reduce launch");
+    // every rank's MLP share on xhat, then h += sum
+    if ((st = run_colpar(xhat, W1t, b1, Y_ws, T, 0, M, H, F, T, TP_BF16, stream)) != TP_OK) return st;
+    if ((st = run_rowpar(reinterpret_cast<const void *const *>(Y_ws), W2t, parts, T, 0, M, H, F, T, TP_BF16,
+                         stream)) != TP_OK)
+        return st;
+    e = tpk::launch_shard_reduce(parts, T, h, h, nullptr, M, H, false, TP_RMS_EPS, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "tp_layer_fwd reduce launch");
+}
+
 tp_status tp_shard_reduce(const float *const *partials, int32_t T, const float *residual, float *out_f32,
                           void *out_bf16, int64_t M, int64_t H, uint32_t flags, hipStream_t stream)
 {

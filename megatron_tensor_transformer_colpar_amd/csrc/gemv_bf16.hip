@@ -5,9 +5,10 @@
 // along in MFMA tiles padded to 16 tokens (the MFMA units have orders of
 // magnitude of headroom at this intensity, VALU would not at M = 32).
 //
-// Layout: a workgroup owns 16 weight rows [n0, n0+16) and KS waves; wave w
-// streams the K range [w*K/KS, (w+1)*K/KS) of those rows with 16-byte loads
-// (16 rows x 64 contiguous bytes per load instruction) and multiplies them
+// Layout: a workgroup owns 16 weight rows [n0, n0+16) and KS (up to 16)
+// waves; wave w streams the K range [w*K/KS, (w+1)*K/KS) of those rows with
+// 16-byte loads (16 rows x 64 contiguous bytes per load instruction), in
+// chunks whose loads are all issued before their MFMAs, and multiplies them
 // with v_mfma_f32_16x16x32_bf16 against 16-token tiles of X (tokens past M
 // read as zero through the buffer resource).  The KS partial tiles are then
 // summed in LDS in fixed order (deterministic, no atomics) and the epilogue
@@ -29,7 +30,11 @@ struct GemvDev {
     int M, N, K;
 };
 
-template <int EPI, int MT, int KS, int U>
+// NT loads (cache policy "nt") for the weight stream, which is read once,
+// so the reused token rows stay resident in L2.
+constexpr int kStreamPolicy = 2;
+
+template <int EPI, int MT, int KS, int CHUNK>
 __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
 {
     __shared__ float red[KS][MT * 4 * 64];
@@ -58,21 +63,29 @@ __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{};
 
-    for (int k = 0; k < Kw; k += 32 * U) {
-        u32x4 wv[U], xv[U][MT];
+    // Every load of a chunk is issued before its first MFMA, so a wave keeps
+    // CHUNK KiB of weights in flight and the KS waves of the CU together
+    // cover the HBM latency.
+    for (int k = 0; k < Kw; k += 32 * CHUNK) {
+        u32x4 wv[CHUNK], xv[CHUNK][MT];
         const uint32_t soff = (uint32_t)k * 2;
 #pragma unroll
-        for (int u = 0; u < U; ++u) wv[u] = buf_load16(wsrc, w_voff + u * 64, soff);
+        for (int c = 0; c < CHUNK; ++c)
+            wv[c] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, (int)(w_voff + c * 64), (int)soff, kStreamPolicy);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int c = 0; c < CHUNK; ++c)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) xv[u][mt] = buf_load16(xsrc, x_voff[mt] + u * 64, soff);
+            for (int mt = 0; mt < MT; ++mt) xv[c][mt] = buf_load16(xsrc, x_voff[mt] + c * 64, soff);
+        // With two token tiles the scheduler would interleave MFMAs (and
+        // their waits) into the load block and cap the bytes in flight; with
+        // one tile its interleave measured faster, so it is left alone.
+        if (MT == 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int c = 0; c < CHUNK; ++c)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, wv[u]),
-                                                                   __builtin_bit_cast(bf16x8v, xv[u][mt]),
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, wv[c]),
+                                                                   __builtin_bit_cast(bf16x8v, xv[c][mt]),
                                                                    acc[mt], 0, 0, 0);
     }
 
@@ -101,21 +114,33 @@ __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
     }
 }
 
+template <int EPI, int MT, int KS>
+hipError_t launch_ks(const GemvDev &g, int batch, hipStream_t s)
+{
+    const dim3 grid((unsigned)(g.N / 16), (unsigned)batch);
+    const int steps = g.K / KS / 32;  // MFMA k-steps per wave
+#ifndef TP_GEMV_MAX_CHUNK
+#define TP_GEMV_MAX_CHUNK 8
+#endif
+    if (TP_GEMV_MAX_CHUNK >= 16 && MT == 1 && steps % 16 == 0)
+        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, KS, 16>), grid, dim3(KS * 64), 0, s, g);
+    else if (steps % 8 == 0)
+        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, KS, 8>), grid, dim3(KS * 64), 0, s, g);
+    else
+        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, KS, 2>), grid, dim3(KS * 64), 0, s, g);
+    return hipGetLastError();
+}
+
 template <int EPI, int MT>
 hipError_t launch_mt(const GemvDev &g, int batch, hipStream_t s)
 {
-    const dim3 grid((unsigned)(g.N / 16), (unsigned)batch);
-    // Split K over as many waves as keeps >= 128 elements per wave and a
-    // 128-element (U = 4) or 64-element (U = 2) inner step.
-    if (g.K % (8 * 128) == 0)
-        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, 8, 4>), grid, dim3(8 * 64), 0, s, g);
-    else if (g.K % (4 * 128) == 0)
-        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, 4, 4>), grid, dim3(4 * 64), 0, s, g);
-    else if (g.K % (2 * 128) == 0)
-        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, 2, 4>), grid, dim3(2 * 64), 0, s, g);
-    else
-        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, 1, 2>), grid, dim3(64), 0, s, g);
-    return hipGetLastError();
+    // Split K over the most waves (16, 8 or 4) that still leaves each wave
+    // at least 256 elements and an even number of 32-wide k-steps; K is a
+    // multiple of 64, so a single wave always works.
+    if (g.K % (16 * 64) == 0 && g.K / 16 >= 256) return launch_ks<EPI, MT, 16>(g, batch, s);
+    if (g.K % (8 * 64) == 0 && g.K / 8 >= 256) return launch_ks<EPI, MT, 8>(g, batch, s);
+    if (g.K % (4 * 64) == 0 && g.K / 4 >= 256) return launch_ks<EPI, MT, 4>(g, batch, s);
+    return launch_ks<EPI, MT, 1>(g, batch, s);
 }
 
 }  // namespace

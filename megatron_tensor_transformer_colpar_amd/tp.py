@@ -49,8 +49,9 @@ _pp = ctypes.POINTER(_vp)
 raw.tp_colpar_gelu_group.argtypes = [_vp, _vp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
 raw.tp_rowpar_partial_group.argtypes = [_pp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
 raw.tp_mlp_group_fwd.argtypes = [_vp, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
+raw.tp_layer_fwd.argtypes = [_vp, _vp, _pp, _vp, _i64, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _vp]
 for _f in (raw.tp_colpar_gelu, raw.tp_rowpar_partial, raw.tp_shard_reduce, raw.tp_mlp_shard_fwd,
-           raw.tp_colpar_gelu_group, raw.tp_rowpar_partial_group, raw.tp_mlp_group_fwd):
+           raw.tp_colpar_gelu_group, raw.tp_rowpar_partial_group, raw.tp_mlp_group_fwd, raw.tp_layer_fwd):
     _f.restype = ctypes.c_int
 raw.tp_last_error.argtypes = []
 raw.tp_last_error.restype = ctypes.c_char_p
@@ -58,8 +59,8 @@ raw.tp_version.argtypes = []
 raw.tp_version.restype = ctypes.c_char_p
 
 EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_shard_fwd",
-           "tp_colpar_gelu_group", "tp_rowpar_partial_group", "tp_mlp_group_fwd", "tp_last_error",
-           "tp_version")
+           "tp_colpar_gelu_group", "tp_rowpar_partial_group", "tp_mlp_group_fwd", "tp_layer_fwd",
+           "tp_last_error", "tp_version")
 
 
 class TPError(RuntimeError):
@@ -138,3 +139,8 @@ def tp_rowpar_partial_group(Y_ws, W2t, Z_parts, M, H, F, T, dt=TP_BF16, stream=N
 def tp_mlp_group_fwd(X, W1t, b1, W2t, Y_ws, Z_parts, M, H, F, T, dt=TP_BF16, stream=None):
     _check(raw.tp_mlp_group_fwd(_ptr(X), _ptr(W1t), _ptr(b1), _ptr(W2t), _arr(Y_ws), _arr(Z_parts), M, H, F, T,
                                 dt, _stream(stream)))
+
+
+def tp_layer_fwd(h, xhat, ctx, Wot, A, W1t, b1, W2t, Y_ws, parts, M, H, F, T, stream=None):
+    _check(raw.tp_layer_fwd(_ptr(h), _ptr(xhat), _arr(ctx), _ptr(Wot), A, _ptr(W1t), _ptr(b1), _ptr(W2t),
+                            _arr(Y_ws), _arr(parts), M, H, F, T, _stream(stream)))

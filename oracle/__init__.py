@@ -184,3 +184,23 @@ def mlp_shard(X, W1, b1, W2, T: int, i: int):
     """Rank i's share: (Y_i, Z_i) with Z_i its row-parallel partial."""
     Y_i = colpar_gelu(X, W1, b1, T, i)
     return Y_i, rowpar_partial(Y_i, W2, T, i)
+
+
+def layer_fwd(h, ctx_shards, Wo, W1, b1, W2, T: int, eps: float):
+    """One block of the layer stack on the residual stream h [M, H] (fp64).
+
+    Both all-reduces sit on residual paths ("Tensor parallelism" guide,
+    "Walking through a transformer block"); one follows the head-sharded
+    attention output projection, one the MLP ("Slice the matrix itself",
+    "All-Reduce Synchronization"):
+      h  <- h + sum_i ctx_i . Wo[A_i, :]          (attention out-projection)
+      xh <- h / rms(h)   (row RMS with eps; not from the pages: it keeps a deep
+                          stack with no normalisation layer finite)
+      h  <- h + sum_i GeLU(xh . W1[:, C_i] + b1[C_i]) . W2[C_i, :]
+    ctx_shards: T arrays [M, A/T] (rank i's heads); Wo [A, H]; W1 [H, F];
+    W2 [F, H].  Returns (h_out, xh).
+    """
+    P = np.stack([rowpar_partial(ctx_shards[i], Wo, T, i) for i in range(T)])
+    h1, xh = shard_reduce(P, h, rms_eps=eps)
+    Z = np.stack([mlp_shard(xh, W1, b1, W2, T, i)[1] for i in range(T)])
+    return shard_reduce(Z, h1), xh

@@ -194,3 +194,32 @@ def test_group_halves_reject_and_accept_empty():
     assert tp.raw.tp_colpar_gelu_group(P[0], P[1], P[2], Y, 0, 64, 256, 2, BF16, None) == tp.TP_OK
     assert tp.raw.tp_rowpar_partial_group(Y, P[4], Z, 0, 64, 256, 2, BF16, None) == tp.TP_OK
     assert group(M=0) == tp.TP_OK
+
+
+def layer(h=P[10], xh=P[11], ctx=None, Wo=P[1], A=256, W1=P[2], b=P[3], W2=P[4], Y=None, parts=None,
+          M=4, H=64, F=256, T=2):
+    ctx = arr(P[5], P[5] + 0x100000) if ctx is None else ctx
+    Y = arr(P[6], P[7]) if Y is None else Y
+    parts = arr(P[8], P[9]) if parts is None else parts
+    return tp.raw.tp_layer_fwd(h, xh, ctx, Wo, A, W1, b, W2, Y, parts, M, H, F, T, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=None), tp.TP_ERR_NULL),
+    (dict(xh=None), tp.TP_ERR_NULL),
+    (dict(ctx=arr(P[5], None)), tp.TP_ERR_NULL),
+    (dict(Wo=None), tp.TP_ERR_NULL),
+    (dict(A=255), tp.TP_ERR_SHAPE),
+    (dict(A=2 * 96), tp.TP_ERR_UNSUPPORTED),
+    (dict(h=P[10] + 8), tp.TP_ERR_UNSUPPORTED),
+    (dict(xh=P[10] + 64), tp.TP_ERR_ALIAS),           # xhat over h
+    (dict(h=P[8]), tp.TP_ERR_ALIAS),                  # h over a partial
+    (dict(parts=arr(P[8], P[5])), tp.TP_ERR_ALIAS),   # partial over ctx
+])
+def test_layer_rejects(kw, status):
+    assert layer(**kw) == status
+    assert "tp_layer_fwd" in tp.last_error()
+
+
+def test_layer_empty_is_ok():
+    assert layer(M=0) == tp.TP_OK

@@ -224,3 +224,41 @@ def test_oracle_rejects_bad_arguments():
         oracle.colpar_gelu(np.ones((2, 3)), np.ones((3, 4)), None, 2, 2)   # i >= T
     with pytest.raises(ValueError):
         oracle.rowpar_partial(np.ones((2, 3)), np.ones((4, 5)), 2, 0)      # Y_i width
+
+
+# ------------------------------------------------------- layer-stack pins
+def _layer_inputs(rng, M=3, H=16, F=32, A=16, T=4):
+    ctx = [rng.standard_normal((M, A // T)) for _ in range(T)]
+    return (rng.standard_normal((M, H)), ctx, 0.3 * rng.standard_normal((A, H)),
+            0.3 * rng.standard_normal((H, F)), 0.1 * rng.standard_normal(F), 0.3 * rng.standard_normal((F, H)))
+
+
+def test_layer_zero_weights_leave_the_stream_unchanged():
+    rng = np.random.default_rng(20)
+    h, ctx, Wo, W1, b1, W2 = _layer_inputs(rng)
+    out, xh = oracle.layer_fwd(h, ctx, 0 * Wo, W1, b1, 0 * W2, 4, 1e-6)
+    assert np.array_equal(out, h)
+    assert np.allclose(np.sqrt(np.mean(xh ** 2, axis=1)), 1.0, rtol=1e-6)
+
+
+def test_layer_is_independent_of_the_tp_degree():
+    # Sharding does not change the mathematics: T = 1, 2, 4 give the same block.
+    rng = np.random.default_rng(21)
+    h, _, Wo, W1, b1, W2 = _layer_inputs(rng)
+    ctx_full = rng.standard_normal((3, 16))
+    outs = []
+    for T in (1, 2, 4):
+        ctx = [ctx_full[:, i * 16 // T:(i + 1) * 16 // T] for i in range(T)]
+        outs.append(oracle.layer_fwd(h, ctx, Wo, W1, b1, W2, T, 1e-6)[0])
+    assert np.allclose(outs[0], outs[1], rtol=0, atol=1e-12) and np.allclose(outs[0], outs[2], rtol=0, atol=1e-12)
+
+
+def test_layer_against_library_composition():
+    # the same block from numpy's matmul and the pinned GeLU
+    rng = np.random.default_rng(22)
+    h, ctx, Wo, W1, b1, W2 = _layer_inputs(rng)
+    out, _ = oracle.layer_fwd(h, ctx, Wo, W1, b1, W2, 4, 1e-6)
+    h1 = h + np.concatenate(ctx, axis=1) @ Wo
+    xh = h1 / np.sqrt(np.mean(h1 ** 2, axis=1, keepdims=True) + 1e-6)
+    want = h1 + oracle.gelu(xh @ W1 + b1) @ W2
+    assert np.max(np.abs(out - want)) <= 1e-12 * (1 + np.max(np.abs(want)))
