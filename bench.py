@@ -18,6 +18,8 @@ Also reported on the same JSON line:
   decode        rank 0's MLP shard + attention out-projection shard at
                 H=8192, F/T=4096, A/T=1024, M in {1, 8, 32}, rotating over
                 weight sets larger than the last-level cache (HBM GB/s)
+  stack80       80 layers (H=8192, F=32768, A=8192, T=8, whole group per
+                layer) at decode M=8 (weight GB/s) and prefill M=4096 (TFLOP/s)
   cpu_baseline  the fp64 oracle on a bounded sample of the headline rows
   parity        the sampled rows of the last step against the oracle
 
@@ -262,6 +264,65 @@ def decode(args, torch, tp):
     return res
 
 
+def stack80(args, torch, tp):
+    """The 80-layer stack (H=8192, F=32768, A=64x128, T=8), the whole TP group
+    emulated: per layer all 8 ranks' out-projection partials, the reduce into
+    the residual stream (with its row-RMS bf16 copy), all 8 ranks' MLP shares,
+    the second reduce.  Independent seeded weights per layer."""
+    L, H, F, A, T = 80, 8192, 32768, 8192, 8
+    g = torch.Generator(device="cuda").manual_seed(80)
+    layers = []
+    for _ in range(L):
+        layers.append(dict(Wot=(torch.randn(H, A, generator=g, device="cuda") * 0.02).to(torch.bfloat16),
+                           W1t=(torch.randn(F, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16),
+                           b1=(torch.randn(F, generator=g, device="cuda") * 0.01).to(torch.bfloat16),
+                           W2t=(torch.randn(H, F, generator=g, device="cuda") * 0.02).to(torch.bfloat16)))
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"workload": "80 layers, H=8192 F=32768 A=8192 T=8, all 8 ranks per layer"}
+    wbytes = L * (2.0 * (H * A + 2 * F * H + F))
+    for M, steps in ((8, max(3, args.steps // 5)), (4096, 2)):
+        ctx_t = [[torch.randn(M, A // T, generator=g, device="cuda").to(torch.bfloat16) for _ in range(T)]
+                 for _ in range(L)]
+        ctx = [tp.partial_array(c) for c in ctx_t]
+        x0 = torch.randn(M, H, generator=g, device="cuda")
+        h = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        xhat = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+        Y_t = [torch.empty(M, F // T, dtype=torch.bfloat16, device="cuda") for _ in range(T)]
+        P_t = [torch.empty(M, H, dtype=torch.float32, device="cuda") for _ in range(T)]
+        Y, parts = tp.partial_array(Y_t), tp.partial_array(P_t)
+
+        def step():
+            h.copy_(x0)
+            for l, p in enumerate(layers):
+                tp.tp_layer_fwd(h, xhat, ctx[l], p["Wot"], A, p["W1t"], p["b1"], p["W2t"], Y, parts, M, H, F, T,
+                                stream)
+
+        step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        flops = L * (2.0 * M * A * H + 4.0 * M * H * F)
+        e = {"steps": steps, "ms_per_step_group": round(ms, 3), "ms_per_step_per_rank_share": round(ms / T, 3),
+             "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        if M == 8:
+            e["weight_gbs"] = round(wbytes / (ms * 1e-3) / 1e9, 1)
+            e["frac_hbm"] = round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            e["us_per_token"] = round(ms * 1e3 / M, 2)
+        else:
+            e["frac_mfma"] = round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        out["M=%d" % M] = e
+        log("[bench] stack80 M=%d: %s" % (M, e))
+        assert bool(torch.isfinite(h).all()), "stack80 produced non-finite values"
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(args, hl):
     import numpy as np
 
@@ -347,6 +408,8 @@ def main():
     if not args.no_extras:
         rec["prefill"] = prefill(args, torch, tp)
         rec["decode"] = decode(args, torch, tp)
+        torch.cuda.empty_cache()
+        rec["stack80"] = stack80(args, torch, tp)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, hl)
     print(json.dumps(rec), flush=True)
