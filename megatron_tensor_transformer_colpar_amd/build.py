@@ -42,6 +42,15 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_no_missing_stubs(lib: str) -> None:
+    """Fail if the host pass dropped a kernel's launch stub (the library would
+    link, then refuse to load)."""
+    r = subprocess.run(["nm", "-u", "-C", lib], capture_output=True, text=True)
+    missing = [l.strip() for l in r.stdout.splitlines() if "tpk::" in l]
+    if missing:
+        raise RuntimeError("libtpcolpar.so references undefined library symbols:\n" + "\n".join(missing))
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libtpcolpar.so; returns its path."""
     os.makedirs(OUT_DIR, exist_ok=True)
@@ -52,6 +61,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
+    _check_no_missing_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -3,11 +3,12 @@
 // with the epilogue fused: either + bias, GeLU, bf16 store (column-parallel
 // up-projection) or an fp32 store (row-parallel partial).
 //
-// Design for gfx950 (CDNA4), one 256-thread workgroup (4 waves, one per
-// SIMD) per BM x BN output tile:
-//  * v_mfma_f32_32x32x16_bf16: each wave owns a (BM/2) x (BN/2) block of
-//    32x32 accumulator tiles held in AGPRs; 32x32 tiles need half the LDS
-//    fragment traffic of 16x16 tiles per flop.
+// Design for gfx950 (CDNA4), one workgroup per BM x BN output tile, NW waves
+// (8 for the large tiles: two per SIMD, so one wave's MFMAs keep issuing
+// while the other waits on the issue of its loads; 4 for the small tile):
+//  * v_mfma_f32_32x32x16_bf16: the waves form a 2 x NW/2 grid, each owning a
+//    (BM/2) x (2*BN/NW) block of 32x32 accumulator tiles; 32x32 tiles need
+//    half the LDS fragment traffic of 16x16 tiles per flop.
 //  * K advances in BK-wide slices (BK = 64: 128 B per row, or 32) through a
 //    ring of S LDS stages filled by direct global->LDS DMA (buffer_load ...
 //    lds, 16 B per lane): no staging registers, no ds_write, and S-1 slices
@@ -60,14 +61,15 @@ __host__ __device__ constexpr int wait_vm_lgkm0(int vm)
     return (vm & 0xF) | (0x7 << 4) | (0x0 << 8) | ((vm >> 4) << 14);
 }
 
-template <int BM, int BN, int BK, int S>
+template <int BM, int BN, int BK, int S, int NW>
 struct Cfg {
-    static constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile (2 x 2 waves)
+    static constexpr int WN = NW / 2;                  // waves along N (2 along M)
+    static constexpr int WTM = BM / 2, WTN = BN / WN;  // wave tile
     static constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA tiles per wave
     static constexpr int CH = BK / 8;                  // 16-byte chunks per LDS row
     static constexpr int RB = 64 / CH;                 // rows per 1 KiB DMA block
     static constexpr int KQ = BK / 16;                 // MFMA k-steps per slice
-    static constexpr int A_LD = BM / RB / 4, B_LD = BN / RB / 4;  // DMA instrs per wave per slice
+    static constexpr int A_LD = BM / RB / NW, B_LD = BN / RB / NW;  // DMA instrs per wave per slice
     static constexpr int LOADS = A_LD + B_LD;          // per thread per slice
     static constexpr int STAGE = (BM + BN) * CH;       // 16-byte slots per stage
     static_assert(BK == 32 || BK == 64, "BK");
@@ -76,10 +78,10 @@ struct Cfg {
     static_assert((S - 2) * LOADS <= 63, "vmcnt range");
 };
 
-template <int BM, int BN, int BK, int S, bool IL, int EPI>
-__global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmDev g)
+template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI>
+__global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 {
-    using C_ = Cfg<BM, BN, BK, S>;
+    using C_ = Cfg<BM, BN, BK, S, NW>;
     constexpr int TM = C_::TM, TN = C_::TN, STAGE = C_::STAGE, CH = C_::CH, RB = C_::RB, KQ = C_::KQ;
     __shared__ u32x4 st0[STAGE];
     __shared__ u32x4 st1[STAGE];
@@ -91,7 +93,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmDev g)
     const int lane = t & 63;
     // wave-uniform, kept in an SGPR so the DMA's LDS address (M0) is scalar
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / C_::WN, wn = wave % C_::WN;
 
     int bt, tile_m, tile_n;
     map_tile<8>(blockIdx.x, g.batch, g.tiles_m, g.tiles_n, bt, tile_m, tile_n);
@@ -107,16 +109,16 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmDev g)
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(Bbase + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * 2));
 
-    // DMA geometry: instruction j of wave w fills 1 KiB block (4j + w), i.e.
-    // rows RB(4j + w) .. +RB-1; lane L lands in slot L of the block (row
-    // L/CH, physical chunk L%CH) and so fetches logical chunk
+    // DMA geometry: instruction j of wave w fills 1 KiB block (NW*j + w),
+    // i.e. rows RB(NW*j + w) .. +RB-1; lane L lands in slot L of the block
+    // (row L/CH, physical chunk L%CH) and so fetches logical chunk
     // (L%CH) ^ swz(row).  The swizzle depends on row bits 0..3 only, so it
     // is the same for every j.
     const int drow = wave * RB + lane / CH;
     const int dchunk = (lane % CH) ^ swz<CH>(drow);
     const uint32_t a_voff = (uint32_t)(drow * g.lda * 2 + dchunk * 16);
     const uint32_t b_voff = (uint32_t)(drow * g.ldb * 2 + dchunk * 16);
-    const uint32_t a_jstep = (uint32_t)(4 * RB * g.lda * 2), b_jstep = (uint32_t)(4 * RB * g.ldb * 2);
+    const uint32_t a_jstep = (uint32_t)(NW * RB * g.lda * 2), b_jstep = (uint32_t)(NW * RB * g.ldb * 2);
     const int KT = g.K / BK;
 
     // The row offset stays in the per-lane voffset, which the buffer range
@@ -126,11 +128,11 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmDev g)
         const uint32_t koff = (uint32_t)min(kt, KT - 1) * (BK * 2);
 #pragma unroll
         for (int j = 0; j < C_::A_LD; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(stage + (4 * j + wave) * 64), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(stage + (NW * j + wave) * 64), 16,
                                                     a_voff + j * a_jstep, koff, 0, 0);
 #pragma unroll
         for (int j = 0; j < C_::B_LD; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (4 * j + wave) * 64), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16,
                                                     b_voff + j * b_jstep, koff, 0, 0);
     };
 
@@ -282,7 +284,7 @@ __global__ void __launch_bounds__(256) gemm_bf16_kernel(GemmDev g)
     }
 }
 
-template <int BM, int BN, int BK, int S, bool IL>
+template <int BM, int BN, int BK, int S, int NW, bool IL>
 hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
 {
     GemmDev g;
@@ -302,11 +304,11 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
     g.batch = a.batch;
     g.tiles_m = (int)((a.M + BM - 1) / BM);
     g.tiles_n = (int)((a.N + BN - 1) / BN);
-    const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(256);
+    const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(NW * 64);
     if (epi == EPI_BIAS_GELU)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, IL, EPI_BIAS_GELU>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU>), grid, block, 0, s, g);
     else
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, IL, EPI_STORE_F32>), grid, block, 0, s, g);
+        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI_STORE_F32>), grid, block, 0, s, g);
     return hipGetLastError();
 }
 
@@ -322,13 +324,13 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, Epilogue epi, int num_cu, hipStre
 #define TP_GEMM_IL true
 #endif
 #ifndef TP_GEMM_BIG
-#define TP_GEMM_BIG 256, 256, 64, 2
+#define TP_GEMM_BIG 256, 256, 64, 2, 8
 #endif
 #ifndef TP_GEMM_MID
-#define TP_GEMM_MID 256, 128, 64, 3
+#define TP_GEMM_MID 256, 128, 64, 3, 8
 #endif
 #ifndef TP_GEMM_SMALL
-#define TP_GEMM_SMALL 128, 128, 64, 3
+#define TP_GEMM_SMALL 128, 128, 64, 3, 4
 #endif
     if (tiles(256, 256) >= num_cu) return launch_cfg<TP_GEMM_BIG, TP_GEMM_IL>(a, epi, s);
     if (tiles(256, 128) >= num_cu) return launch_cfg<TP_GEMM_MID, TP_GEMM_IL>(a, epi, s);
