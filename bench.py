@@ -20,6 +20,8 @@ Also reported on the same JSON line:
                 weight sets larger than the last-level cache (HBM GB/s)
   stack80       80 layers (H=8192, F=32768, A=8192, T=8, whole group per
                 layer) at decode M=8 (weight GB/s) and prefill M=4096 (TFLOP/s)
+  hipblaslt_context  the column-parallel launches next to torch.matmul
+                (hipBLASLt) on the same shapes, same GPU, same run
   cpu_baseline  the fp64 oracle on a bounded sample of the headline rows
   parity        the sampled rows of the last step against the oracle
 
@@ -210,6 +212,48 @@ def prefill(args, torch, tp):
     return out
 
 
+def hipblaslt_context(args, torch, tp):
+    """The library's column-parallel launches next to hipBLASLt (torch.matmul,
+    bf16 out, no bias or GeLU) on the same shapes, timed alternately on the
+    same GPU.  Context for the roofline figures only; never the reported value."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(f, reps=20):
+        for _ in range(3):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def bf(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+    out = {}
+    for label, M, H, F, T in (("gpt_block_shard column-parallel, 4 shards", 2048, 4096, 16384, 4),
+                              ("prefill column-parallel, rank 0", 8192, 8192, 4096, 1)):
+        X, W1t, b1 = bf(M, H), bf(F, H, std=0.02), bf(F, std=0.01)
+        Ys = [torch.empty(M, F // T, dtype=torch.bfloat16, device="cuda") for _ in range(T)]
+        W1 = W1t.t().contiguous()
+        lib = lambda: tp.tp_colpar_gelu_group(X, W1t, b1, Ys, M, H, F, T, tp.TP_BF16, stream)
+        ref = lambda: torch.matmul(X, W1)
+        a, b = [], []
+        for _ in range(2):
+            a.append(timed(lib))
+            b.append(timed(ref))
+        fl = 2.0 * M * H * F
+        out[label] = {"library_tflops": round(fl / (min(a) * 1e-3) / 1e12, 1),
+                      "hipblaslt_tflops": round(fl / (min(b) * 1e-3) / 1e12, 1)}
+        del X, W1t, b1, Ys, W1
+    log("[bench] hipBLASLt context: %s" % out)
+    return out
+
+
 def decode(args, torch, tp):
     # rank 0 at H=8192, F/T=4096, A/T=1024; R weight sets rotate so that every
     # call streams its weights from HBM (R * 144 MiB is > 4x the 256 MB MALL).
@@ -242,6 +286,18 @@ def decode(args, torch, tp):
         for k in range(2 * R):
             step(sets[k % R])
         n = max(2 * R, args.steps)
+        # the step itself, with events only around the whole run (an event
+        # between two launches adds a gap of its own) ...
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(n):
+            step(sets[k % R])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        # ... and a second run with an event before each launch for the
+        # per-kernel durations
         tl = Timeline(torch)
         torch.cuda.synchronize()
         tl.mark(None)
@@ -249,7 +305,6 @@ def decode(args, torch, tp):
             step(sets[k % R], tl)
         tl.mark(None)
         torch.cuda.synchronize()
-        ms = tl.marks[0][1].elapsed_time(tl.marks[-1][1]) / n
         mlp_bytes = 2.0 * (Fs * H * 2 + Fs) + M * H * 2 + M * H * 4
         op_bytes = 2.0 * H * As + M * As * 2 + M * H * 4
         d = {k: sum(v) / len(v) for k, v in tl.durations().items()}
@@ -365,6 +420,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline step only (for profiling)")
+    ap.add_argument("--context-only", action="store_true",
+                    help="only the library-vs-hipBLASLt comparison (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -378,6 +435,9 @@ def main():
     from megatron_tensor_transformer_colpar_amd import inputs, tp
 
     torch.cuda.set_device(0)
+    if args.context_only:
+        print(json.dumps({"hipblaslt_context": hipblaslt_context(args, torch, tp)}), flush=True)
+        return
     if args.copy_calibration:
         # a plain copy of known size: 1 GiB read + 1 GiB written per launch
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -410,6 +470,7 @@ def main():
         rec["decode"] = decode(args, torch, tp)
         torch.cuda.empty_cache()
         rec["stack80"] = stack80(args, torch, tp)
+        rec["hipblaslt_context"] = hipblaslt_context(args, torch, tp)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, hl)
     print(json.dumps(rec), flush=True)

@@ -5,14 +5,16 @@
 // along in MFMA tiles padded to 16 tokens (the MFMA units have orders of
 // magnitude of headroom at this intensity, VALU would not at M = 32).
 //
-// Layout: a workgroup owns 16 weight rows [n0, n0+16) and KS (up to 16)
-// waves; wave w streams the K range [w*K/KS, (w+1)*K/KS) of those rows with
-// 16-byte loads (16 rows x 64 contiguous bytes per load instruction), in
-// chunks whose loads are all issued before their MFMAs, and multiplies them
-// with v_mfma_f32_16x16x32_bf16 against 16-token tiles of X (tokens past M
-// read as zero through the buffer resource).  The KS partial tiles are then
-// summed in LDS in fixed order (deterministic, no atomics) and the epilogue
-// (bias + GeLU -> bf16, or fp32) is applied.
+// Layout: a workgroup owns 16 weight rows [n0, n0+16) and KS (1, 4 or 8)
+// waves; wave w streams the K range [w*K/KS, (w+1)*K/KS) of those rows and
+// multiplies it with v_mfma_f32_16x16x32_bf16 against 16-token tiles of X
+// (tokens past M read as zero through the buffer resource).  The KS partial
+// tiles are then summed in LDS in fixed order (deterministic, no atomics)
+// and the epilogue (bias + GeLU -> bf16, or fp32) is applied.  Two stream
+// kernels: gemv_seg_kernel (contiguous 256-byte row segments per load,
+// regrouped through LDS) whenever each wave's range is a multiple of 128
+// elements, else gemv_bf16_kernel (16 rows x 64 bytes per load straight into
+// the fragments).
 #include "device_common.h"
 #include "tp_kernels.h"
 
@@ -114,17 +116,121 @@ __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
     }
 }
 
+// Segmented stream (used whenever a wave's K range is a multiple of 128):
+// every weight load instruction reads 4 rows x 256 contiguous bytes (lane l:
+// row 4i + l/16, bytes 16*(l%16) of the segment); HBM serves that at ~6.5
+// TB/s where the 16-rows-x-64-bytes pattern above reaches ~5.3 (pure-read
+// measurements on MI355X).  Each wave moves a 4 KiB unit (16 rows x 128 k)
+// through its own 4 KiB LDS slot into the 16x16x32 fragment order, with no
+// workgroup barrier: the 16-byte slot is i*64 + a*16 + (b ^ (4i + a)) on the
+// write (instruction i, lane (a, b)) and (r/4)*64 + (r%4)*16 + ((4s + g) ^ r)
+// on the read (k-step s, lane (g, r)), conflict-free both ways.  A lane's
+// fragment holds the same k values as in gemv_bf16_kernel, so for the same
+// split of K the sums are formed in the same order.  D units (loads of
+// weights and tokens) are kept in flight per wave.
+template <int EPI, int MT, int KS, int D>
+__global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
+{
+    __shared__ u32x4 ulds[KS][256];
+    __shared__ float red[KS][MT * 4 * 64];
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int n0 = blockIdx.x * 16;
+    const int bt = blockIdx.y;
+    const int Kw = g.K / KS;
+    const int kbeg = w * Kw;
+    const int units = Kw / 128;
+
+    const __amdgpu_buffer_rsrc_t wsrc =
+        make_rsrc(g.W[bt] + (int64_t)n0 * g.ldw, (uint32_t)(16 * g.ldw * 2));
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(g.X[bt], (uint32_t)((int64_t)g.M * g.ldx * 2));
+
+    const int a = lane >> 4, b = lane & 15;
+    uint32_t w_voff[4];
+    int wslot[4], rslot[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w_voff[i] = (uint32_t)(((4 * i + a) * g.ldw + kbeg) * 2 + b * 16);
+        wslot[i] = i * 64 + a * 16 + (b ^ (4 * i + a));
+        rslot[i] = (b >> 2) * 64 + (b & 3) * 16 + ((4 * i + a) ^ b);
+    }
+    uint32_t x_voff[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) x_voff[mt] = (uint32_t)(((mt * 16 + b) * g.ldx + kbeg + 8 * a) * 2);
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{};
+
+    u32x4 wv[D][4], xv[D][4][MT];
+    auto issue = [&](int u, int d) __attribute__((always_inline)) {
+        const int so = u * 256;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[d][i] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, (int)w_voff[i], so, kStreamPolicy);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) xv[d][s][mt] = buf_load16(xsrc, x_voff[mt] + s * 64, (uint32_t)so);
+    };
+    auto step = [&](int u, int d) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ulds[w][wslot[i]] = wv[d][i];
+        u32x4 f[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) f[s] = ulds[w][rslot[s]];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, f[s]),
+                                                                   __builtin_bit_cast(bf16x8v, xv[d][s][mt]),
+                                                                   acc[mt], 0, 0, 0);
+        if (u + D < units) issue(u + D, d);
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (d < units) issue(d, d);
+    for (int u = 0; u < units; u += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (u + d < units) step(u + d, d);
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[w][(mt * 4 + v) * 64 + lane] = acc[mt][v];
+    __syncthreads();
+
+    void *const Cb = g.C[bt];
+    const __bf16 *const bias = g.bias[bt];
+    for (int idx = t; idx < MT * 4 * 64; idx += KS * 64) {
+        float s = red[0][idx];
+#pragma unroll
+        for (int j = 1; j < KS; ++j) s += red[j][idx];
+        const int l = idx & 63, v = (idx >> 6) & 3, mt = idx >> 8;
+        const int m = mt * 16 + (l & 15);
+        const int n = n0 + 4 * (l >> 4) + v;
+        if (m >= g.M) continue;
+        if (EPI == EPI_BIAS_GELU) {
+            const float bb = bias ? (float)bias[n] : 0.0f;
+            static_cast<__bf16 *>(Cb)[(int64_t)m * g.ldc + n] = (__bf16)gelu_tanh(s + bb);
+        } else {
+            static_cast<float *>(Cb)[(int64_t)m * g.ldc + n] = s;
+        }
+    }
+}
+
 template <int EPI, int MT, int KS>
 hipError_t launch_ks(const GemvDev &g, int batch, hipStream_t s)
 {
     const dim3 grid((unsigned)(g.N / 16), (unsigned)batch);
+    if ((g.K / KS) % 128 == 0) {
+        hipLaunchKernelGGL((gemv_seg_kernel<EPI, MT, KS, 2>), grid, dim3(KS * 64), 0, s, g);
+        return hipGetLastError();
+    }
     const int steps = g.K / KS / 32;  // MFMA k-steps per wave
-#ifndef TP_GEMV_MAX_CHUNK
-#define TP_GEMV_MAX_CHUNK 8
-#endif
-    if (TP_GEMV_MAX_CHUNK >= 16 && MT == 1 && steps % 16 == 0)
-        hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, KS, 16>), grid, dim3(KS * 64), 0, s, g);
-    else if (steps % 8 == 0)
+    if (steps % 8 == 0)
         hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, KS, 8>), grid, dim3(KS * 64), 0, s, g);
     else
         hipLaunchKernelGGL((gemv_bf16_kernel<EPI, MT, KS, 2>), grid, dim3(KS * 64), 0, s, g);
@@ -134,10 +240,10 @@ hipError_t launch_ks(const GemvDev &g, int batch, hipStream_t s)
 template <int EPI, int MT>
 hipError_t launch_mt(const GemvDev &g, int batch, hipStream_t s)
 {
-    // Split K over the most waves (16, 8 or 4) that still leaves each wave
-    // at least 256 elements and an even number of 32-wide k-steps; K is a
-    // multiple of 64, so a single wave always works.
-    if (g.K % (16 * 64) == 0 && g.K / 16 >= 256) return launch_ks<EPI, MT, 16>(g, batch, s);
+    // Split K over the most waves (8 or 4) that still leaves each wave at
+    // least 256 elements and an even number of 32-wide k-steps; K is a
+    // multiple of 64, so a single wave always works.  Eight waves per block
+    // with two blocks per CU streamed faster than sixteen with one.
     if (g.K % (8 * 64) == 0 && g.K / 8 >= 256) return launch_ks<EPI, MT, 8>(g, batch, s);
     if (g.K % (4 * 64) == 0 && g.K / 4 >= 256) return launch_ks<EPI, MT, 4>(g, batch, s);
     return launch_ks<EPI, MT, 1>(g, batch, s);
