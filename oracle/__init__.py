@@ -48,11 +48,14 @@ def _bind(path):
     lib.orc_gelu.argtypes = [i64, dp, dp]
     lib.orc_gelu.restype = None
     lib.orc_colpar_gelu.argtypes = [i64, i64, i64, i32, i32, dp, dp, dp, dp]
+    lib.orc_act.argtypes = [i32, i64, dp, dp]
+    lib.orc_colpar_act.argtypes = [i64, i64, i64, i32, i32, i32, dp, dp, dp, dp]
+    lib.orc_colpar_gated.argtypes = [i64, i64, i64, i32, i32, i32, dp, dp, dp, dp, dp, dp]
     lib.orc_rowpar_partial.argtypes = [i64, i64, i64, i32, i32, dp, dp, dp]
     lib.orc_shard_reduce.argtypes = [i32, i64, i64, dp, dp, dp, dp, ctypes.c_double]
     lib.orc_mlp_unsharded.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp]
     for f in (lib.orc_colpar_gelu, lib.orc_rowpar_partial, lib.orc_shard_reduce,
-              lib.orc_mlp_unsharded):
+              lib.orc_mlp_unsharded, lib.orc_act, lib.orc_colpar_act, lib.orc_colpar_gated):
         f.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [i32]
     lib.orc_set_threads.restype = None
@@ -117,6 +120,53 @@ def gelu(x):
     y = np.empty_like(x)
     _load().orc_gelu(x.size, _p(x), _p(y))
     return y
+
+
+ACT_GELU_TANH, ACT_GELU_ERF = 0, 1
+
+
+def act(x, form: int):
+    """Either GeLU form elementwise in fp64: ACT_GELU_TANH (tanh approximation)
+    or ACT_GELU_ERF (exact x * Phi(x))."""
+    x = _f64(x)
+    y = np.empty_like(x)
+    _check(_load().orc_act(int(form), x.size, _p(x), _p(y)), "act")
+    return y
+
+
+def colpar_act(X, W1, b1, T: int, i: int, form: int):
+    """Shard i of T of the column-parallel up-projection with the chosen GeLU form."""
+    X = _f64(X)
+    M, H = X.shape
+    W1 = _f64(W1)
+    if W1.shape[0] != H:
+        raise ValueError("oracle: W1 must be [H, F]")
+    F = W1.shape[1]
+    b1 = None if b1 is None else _f64(b1, (F,))
+    if F % T:
+        raise ValueError("oracle: F % T != 0")
+    Y = np.empty((M, F // T))
+    _check(_load().orc_colpar_act(M, H, F, T, i, int(form), _p(X), _p(W1), _p(b1), _p(Y)), "colpar_act")
+    return Y
+
+
+def colpar_gated(X, Wg, Wu, bg, bu, T: int, i: int, form: int):
+    """Shard i of T of the gated first layer ("Gate/Up"):
+    a(X Wg[:, C_i] + bg[C_i]) * (X Wu[:, C_i] + bu[C_i]), a the chosen GeLU form."""
+    X = _f64(X)
+    M, H = X.shape
+    Wg, Wu = _f64(Wg), _f64(Wu)
+    if Wg.shape[0] != H or Wu.shape != Wg.shape:
+        raise ValueError("oracle: Wg and Wu must both be [H, F]")
+    F = Wg.shape[1]
+    bg = None if bg is None else _f64(bg, (F,))
+    bu = None if bu is None else _f64(bu, (F,))
+    if F % T:
+        raise ValueError("oracle: F % T != 0")
+    Y = np.empty((M, F // T))
+    _check(_load().orc_colpar_gated(M, H, F, T, i, int(form), _p(X), _p(Wg), _p(Wu), _p(bg), _p(bu), _p(Y)),
+           "colpar_gated")
+    return Y
 
 
 def colpar_gelu(X, W1, b1, T: int, i: int):

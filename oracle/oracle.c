@@ -28,7 +28,8 @@
  *  [GUIDE]  "Tensor parallelism" (inference guide): "Concept";
  *           "Walking through a transformer block".
  *  [GELU]   Hendrycks & Gimpel, "Gaussian Error Linear Units (GELUs)",
- *           arXiv:1606.08415, the tanh approximation of x*Phi(x).
+ *           arXiv:1606.08415: the exact form x*Phi(x) and its tanh
+ *           approximation.
  */
 #include <math.h>
 #include <stddef.h>
@@ -49,10 +50,39 @@ static double gelu_tanh(double x)
     return 0.5 * x * (1.0 + tanh(k * (x + 0.044715 * x * x * x)));
 }
 
+/* GeLU, exact form [GELU]: g(x) = x * Phi(x) with Phi the standard normal
+ * CDF, Phi(x) = (1 + erf(x / sqrt 2)) / 2; erf from the C library. */
+static double gelu_erf(double x)
+{
+    return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+}
+
+#define ORC_ACT_GELU_TANH 0
+#define ORC_ACT_GELU_ERF 1
+
+static double act_apply(int32_t act, double x)
+{
+    return act == ORC_ACT_GELU_ERF ? gelu_erf(x) : gelu_tanh(x);
+}
+
+static int act_ok(int32_t act)
+{
+    return act == ORC_ACT_GELU_TANH || act == ORC_ACT_GELU_ERF;
+}
+
 void orc_gelu(int64_t n, const double *x, double *y)
 {
     for (int64_t j = 0; j < n; ++j)
         y[j] = gelu_tanh(x[j]);
+}
+
+/* Either GeLU form, elementwise. */
+int orc_act(int32_t act, int64_t n, const double *x, double *y)
+{
+    if (!act_ok(act) || n < 0 || (n > 0 && (!x || !y))) return ORC_BAD_ARG;
+    for (int64_t j = 0; j < n; ++j)
+        y[j] = act_apply(act, x[j]);
+    return ORC_OK;
 }
 
 static int shard_ok(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i)
@@ -69,11 +99,10 @@ static int shard_ok(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i)
  * The sum runs over h in increasing order and the bias is added last, for
  * every element, so shard outputs equal the matching columns of the
  * unsharded result bit for bit.  b1 may be NULL (no bias). */
-int orc_colpar_gelu(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i,
-                    const double *X, const double *W1, const double *b1,
-                    double *Y_i)
+int orc_colpar_act(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, int32_t act,
+                   const double *X, const double *W1, const double *b1, double *Y_i)
 {
-    if (!shard_ok(M, H, F, T, i) || !X || !W1 || !Y_i) return ORC_BAD_ARG;
+    if (!shard_ok(M, H, F, T, i) || !act_ok(act) || !X || !W1 || !Y_i) return ORC_BAD_ARG;
     const int64_t Fs = F / T, o = (int64_t)i * Fs;
     #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
@@ -86,9 +115,55 @@ int orc_colpar_gelu(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i,
         }
         for (int64_t c = 0; c < Fs; ++c) {
             const double u = b1 ? acc[c] + b1[o + c] : acc[c];
-            Y_i[m * Fs + c] = gelu_tanh(u);
+            Y_i[m * Fs + c] = act_apply(act, u);
         }
         free(acc);
+    }
+    return ORC_OK;
+}
+
+int orc_colpar_gelu(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i,
+                    const double *X, const double *W1, const double *b1,
+                    double *Y_i)
+{
+    return orc_colpar_act(M, H, F, T, i, ORC_ACT_GELU_TANH, X, W1, b1, Y_i);
+}
+
+/* Gated first layer: the pages call the first linear layer "Gate/Up" and
+ * split it by columns like W1 ([SLICE] "Column-Parallel & Row-Parallel
+ * GEMMs").  Read as a gate and an up projection of the same width, both
+ * split into the same column blocks, combined elementwise (so, like GeLU,
+ * the combination commutes with the split):
+ *   Y_i[m][c] = a( sum_h X[m][h] Wg[h][o+c] + bg[o+c] )
+ *             *  ( sum_h X[m][h] Wu[h][o+c] + bu[o+c] ),   o = i*F/T,
+ * with a the chosen GeLU form.  Wg, Wu are [H][F]; bg, bu may be NULL.
+ * Each sum runs over h in increasing order, the bias is added last. */
+int orc_colpar_gated(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, int32_t act,
+                     const double *X, const double *Wg, const double *Wu,
+                     const double *bg, const double *bu, double *Y_i)
+{
+    if (!shard_ok(M, H, F, T, i) || !act_ok(act) || !X || !Wg || !Wu || !Y_i) return ORC_BAD_ARG;
+    const int64_t Fs = F / T, o = (int64_t)i * Fs;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        double *g = (double *)calloc((size_t)Fs, sizeof(double));
+        double *u = (double *)calloc((size_t)Fs, sizeof(double));
+        for (int64_t h = 0; h < H; ++h) {
+            const double x = X[m * H + h];
+            const double *wg = Wg + h * F + o;
+            const double *wu = Wu + h * F + o;
+            for (int64_t c = 0; c < Fs; ++c) {
+                g[c] += x * wg[c];
+                u[c] += x * wu[c];
+            }
+        }
+        for (int64_t c = 0; c < Fs; ++c) {
+            const double gate = bg ? g[c] + bg[o + c] : g[c];
+            const double up = bu ? u[c] + bu[o + c] : u[c];
+            Y_i[m * Fs + c] = act_apply(act, gate) * up;
+        }
+        free(g);
+        free(u);
     }
     return ORC_OK;
 }

@@ -67,6 +67,51 @@ def test_gelu_high_precision_values():
         assert abs(g - r) <= 8 * np.finfo(np.float64).eps * (1 + abs(x))
 
 
+# -------------------------------------- exact GeLU (x * Phi(x), erf form)
+ERF, TANH = oracle.ACT_GELU_ERF, oracle.ACT_GELU_TANH
+
+
+def test_gelu_erf_textbook_values():
+    # g(x) = x * Phi(x): Phi(1) = 0.8413447460685429 and the two-sided 95%
+    # normal quantile Phi(1.959963984540054) = 0.975 are table values.
+    g1 = oracle.act(np.array([1.0, -1.0]), ERF)
+    assert abs(g1[0] - 0.8413447460685429) < 2e-16
+    assert abs(g1[1] - (-(1.0 - 0.8413447460685429))) < 2e-16
+    q = 1.959963984540054
+    assert abs(oracle.act(np.array([q]), ERF)[0] / q - 0.975) < 1e-15
+
+
+def test_gelu_erf_odd_part_identity_and_limits():
+    # Phi(x) + Phi(-x) = 1, so g(x) - g(-x) = x.
+    x = np.linspace(-10, 10, 40001)
+    d = oracle.act(x, ERF) - oracle.act(-x, ERF)
+    assert np.max(np.abs(d - x) / (1 + np.abs(x))) < 4e-15
+    g = oracle.act(np.array([0.0, 40.0, -40.0, 1e-8]), ERF)
+    assert g[0] == 0.0 and g[1] == 40.0 and abs(g[2]) < 1e-300
+    assert abs(g[3] / 1e-8 - 0.5) < 1e-7
+
+
+def test_gelu_erf_high_precision_values():
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 40
+    xs = [-6.0, -3.0, -1.0, -0.5, -1e-3, 1e-3, 0.5, 2.0, 3.0, 7.25]
+    ref = [float(mp.mpf(x) * (1 + mp.erf(mp.mpf(x) / mp.sqrt(2))) / 2) for x in xs]
+    got = oracle.act(np.array(xs), ERF)
+    for x, r, g in zip(xs, ref, got):
+        assert abs(g - r) <= 8 * np.finfo(np.float64).eps * (1 + abs(x))
+
+
+def test_gelu_forms_differ_by_the_published_bound():
+    # The tanh form's largest deviation from x*Phi(x) is 4.73e-4 at |x| ~ 2.70,
+    # and the tanh entry points agree with each other bit for bit.
+    x = np.linspace(-10, 10, 200001)
+    t, e = oracle.act(x, TANH), oracle.act(x, ERF)
+    assert np.array_equal(t, oracle.gelu(x))
+    err = np.abs(t - e)
+    assert 4.70e-4 < err.max() < 4.76e-4
+    assert abs(abs(x[err.argmax()]) - 2.70) < 0.01
+
+
 # ------------------------------------------------------ column-parallel pins
 def _rand(rng, *shape):
     return rng.standard_normal(shape)
@@ -116,6 +161,79 @@ def test_colpar_gelu_closed_forms():
     Xr = _rand(rng, M, H)
     assert np.array_equal(oracle.colpar_gelu(Xr, W1, None, T, 0),
                           oracle.colpar_gelu(Xr, W1, np.zeros(F), T, 0))
+
+
+def test_colpar_act_erf_matches_library_matmul_and_closed_forms():
+    rng = np.random.default_rng(30)
+    M, H, F, T = 5, 16, 12, 3
+    X, W1, b1 = _rand(rng, M, H), _rand(rng, H, F), _rand(rng, F)
+    for i in range(T):
+        C = slice(i * F // T, (i + 1) * F // T)
+        want = oracle.act(X @ W1[:, C] + b1[C], ERF)
+        got = oracle.colpar_act(X, W1, b1, T, i, ERF)
+        assert np.max(np.abs(got - want)) <= 1e-13 * (1 + np.max(np.abs(want)))
+    # W1 = 0: every row is g(b1[C_i]); the tanh form is colpar_gelu
+    Y = oracle.colpar_act(X, np.zeros((H, F)), b1, T, 2, ERF)
+    assert np.array_equal(Y, np.tile(oracle.act(b1[8:12], ERF), (M, 1)))
+    assert np.array_equal(oracle.colpar_act(X, W1, b1, T, 1, TANH), oracle.colpar_gelu(X, W1, b1, T, 1))
+
+
+# ------------------------------------------------- gated first layer pins
+def test_gated_hand_example():
+    # H = 1, F = 2, T = 2: X = [1; 2], Wg = [1, -1], Wu = [3, 2], no biases.
+    # Rank 0 owns column 0: g(x) * 3x; rank 1 owns column 1: g(-x) * 2x.
+    X, Wg, Wu = np.array([[1.0], [2.0]]), np.array([[1.0, -1.0]]), np.array([[3.0, 2.0]])
+    phi1 = 0.8413447460685429
+    y0 = oracle.colpar_gated(X, Wg, Wu, None, None, 2, 0, ERF)
+    y1 = oracle.colpar_gated(X, Wg, Wu, None, None, 2, 1, ERF)
+    assert abs(y0[0, 0] - phi1 * 3.0) < 1e-15
+    assert abs(y1[0, 0] - (-(1.0 - phi1)) * 2.0) < 1e-15
+    assert abs(y0[1, 0] - oracle.act(np.array([2.0]), ERF)[0] * 6.0) < 1e-15
+
+
+def test_gated_reduces_to_plain_forms():
+    rng = np.random.default_rng(31)
+    M, H, F, T = 6, 10, 8, 2
+    X, Wg, Wu, bg, bu = _rand(rng, M, H), _rand(rng, H, F), _rand(rng, H, F), _rand(rng, F), _rand(rng, F)
+    for form in (TANH, ERF):
+        for i in range(T):
+            C = slice(i * F // T, (i + 1) * F // T)
+            # gate weights 0, gate bias c: a(c) scales the up projection
+            got = oracle.colpar_gated(X, np.zeros((H, F)), Wu, bg, bu, T, i, form)
+            want = oracle.act(bg[C], form) * (X @ Wu[:, C] + bu[C])
+            assert np.max(np.abs(got - want)) <= 1e-13 * (1 + np.max(np.abs(want)))
+            # up weights 0, up bias 1: the plain column-parallel activation
+            got = oracle.colpar_gated(X, Wg, np.zeros((H, F)), bg, np.ones(F), T, i, form)
+            assert np.array_equal(got, oracle.colpar_act(X, Wg, bg, T, i, form))
+    # gate and up are not interchangeable
+    a = oracle.colpar_gated(X, Wg, Wu, bg, bu, T, 0, ERF)
+    b = oracle.colpar_gated(X, Wu, Wg, bu, bg, T, 0, ERF)
+    assert np.max(np.abs(a - b)) > 0.1
+
+
+def test_gated_bruteforce_integers():
+    rng = np.random.default_rng(32)
+    M, H, F, T = 3, 5, 6, 3
+    X, Wg, Wu = (rng.integers(-3, 4, s) for s in ((M, H), (H, F), (H, F)))
+    bg, bu = rng.integers(-3, 4, F), rng.integers(-3, 4, F)
+    Fs = F // T
+    for form in (TANH, ERF):
+        for i in range(T):
+            pg = np.array([[sum(int(X[m, h]) * int(Wg[h, i * Fs + c]) for h in range(H)) + int(bg[i * Fs + c])
+                            for c in range(Fs)] for m in range(M)], dtype=np.float64)
+            pu = np.array([[sum(int(X[m, h]) * int(Wu[h, i * Fs + c]) for h in range(H)) + int(bu[i * Fs + c])
+                            for c in range(Fs)] for m in range(M)], dtype=np.float64)
+            assert np.array_equal(oracle.colpar_gated(X, Wg, Wu, bg, bu, T, i, form), oracle.act(pg, form) * pu)
+
+
+def test_gated_shards_concatenate_to_unsharded():
+    rng = np.random.default_rng(33)
+    M, H, F = 4, 12, 16
+    X, Wg, Wu, bg, bu = _rand(rng, M, H), _rand(rng, H, F), _rand(rng, H, F), _rand(rng, F), None
+    full = oracle.colpar_gated(X, Wg, Wu, bg, bu, 1, 0, ERF)
+    for T in (2, 4, 8):
+        cat = np.concatenate([oracle.colpar_gated(X, Wg, Wu, bg, bu, T, i, ERF) for i in range(T)], axis=1)
+        assert np.array_equal(cat, full)
 
 
 # --------------------------------------------------------- row-parallel pins
@@ -218,6 +336,10 @@ def test_reduce_rms_closed_forms():
 
 
 def test_oracle_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.act(np.ones(3), 2)                                         # unknown form
+    with pytest.raises(ValueError):
+        oracle.colpar_gated(np.ones((2, 3)), np.ones((3, 4)), np.ones((3, 5)), None, None, 2, 0, ERF)
     with pytest.raises(ValueError):
         oracle.colpar_gelu(np.ones((2, 3)), np.ones((3, 5)), None, 2, 0)   # F % T
     with pytest.raises(ValueError):

@@ -2,7 +2,8 @@
 
 Each case compiles a copy of ``oracle/oracle.c`` with one plausible mistake (a
 dropped term, a wrong constant or sign, a missing shard offset, a missing bias,
-a skipped partial) and runs every pin of ``test_oracle.py`` against it; at
+a skipped partial, swapped gate and up operands, swapped GeLU forms) and runs
+every pin of ``test_oracle.py`` against it; at
 least one pin has to fail.  Everything runs on the CPU.
 """
 import os
@@ -28,6 +29,14 @@ MUTANTS = {
     "reduce_residual_sign": ("residual[m * H + n] + s", "residual[m * H + n] - s"),
     "rms_no_eps": ("ss / (double)H + eps", "ss / (double)H"),
     "rms_wrong_mean": ("ss / (double)H + eps", "ss / (double)(H + 1) + eps"),
+    "erf_wrong_scale": ("erf(x / sqrt(2.0))", "erf(x * sqrt(2.0))"),
+    "erf_wrong_sign": ("(1.0 + erf(", "(1.0 - erf("),
+    "act_forms_swapped": ("act == ORC_ACT_GELU_ERF ? gelu_erf(x) : gelu_tanh(x)",
+                          "act == ORC_ACT_GELU_ERF ? gelu_tanh(x) : gelu_erf(x)"),
+    "gated_gate_up_swapped": ("act_apply(act, gate) * up", "act_apply(act, up) * gate"),
+    "gated_up_bias_dropped": ("u[c] + bu[o + c]", "u[c]"),
+    "gated_up_missing_shard_offset": ("Wu + h * F + o;", "Wu + h * F;"),
+    "gated_gate_reads_up": ("const double *wg = Wg + h * F + o;", "const double *wg = Wu + h * F + o;"),
 }
 
 
