@@ -395,7 +395,9 @@ def cpu_baseline(args, hl):
         Zr = oracle.shard_reduce(np.stack(zs))
         return time.perf_counter() - t0, Zr
 
-    probe = inputs.row_sample(w.M, 8, seed=1, include_ends=False)
+    # the oracle threads over rows: probe with two rows per thread so that
+    # the rate it measures is the one the full sample will see
+    probe = inputs.row_sample(w.M, max(16, 2 * oracle.max_threads()), seed=1, include_ends=False)
     dt, _ = run(probe)
     n = int(min(w.M, max(8, len(probe) * args.cpu_seconds / max(dt, 1e-3))))
     rows = inputs.row_sample(w.M, n, seed=2)
@@ -420,6 +422,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline step only (for profiling)")
+    ap.add_argument("--sections", default="prefill,decode,stack80,context",
+                    help="comma-separated extra sections to run after the headline step")
     ap.add_argument("--context-only", action="store_true",
                     help="only the library-vs-hipBLASLt comparison (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -465,11 +469,15 @@ def main():
            "config": {"workload": "gpt_block_shard: all 4 TP shards + on-device reduce", "M": w.M, "H": w.H,
                       "F": w.F, "T": w.T, "parallelism": "tp4 emulated on 1 GPU"},
            "roofline": roof, "kernels": kernels, "per_rank": hl["per_rank"]}
-    if not args.no_extras:
+    sections = set() if args.no_extras else set(x for x in args.sections.split(",") if x)
+    if "prefill" in sections:
         rec["prefill"] = prefill(args, torch, tp)
+    if "decode" in sections:
         rec["decode"] = decode(args, torch, tp)
-        torch.cuda.empty_cache()
+    torch.cuda.empty_cache()
+    if "stack80" in sections:
         rec["stack80"] = stack80(args, torch, tp)
+    if "context" in sections:
         rec["hipblaslt_context"] = hipblaslt_context(args, torch, tp)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, hl)

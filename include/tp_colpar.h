@@ -73,6 +73,10 @@ typedef enum {
 
 typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
 
+/* GeLU form ([GELU]): the tanh approximation (what tp_colpar_gelu applies)
+ * or the exact x * Phi(x), Phi the standard normal CDF. */
+typedef enum { TP_GELU_TANH = 0, TP_GELU_ERF = 1 } tp_act;
+
 /* Largest TP degree: TP stays inside one 8-GPU node ([SLICE] "Strict
  * NVLink Domain Constraint"; [GUIDE] "Trade-off"). */
 #define TP_MAX_T 8
@@ -149,6 +153,34 @@ tp_status tp_rowpar_partial(const void *Y_i, const void *W2t, float *Z_i,
 tp_status tp_shard_reduce(const float *const *partials, int32_t T, const float *residual,
                           float *out_f32, void *out_bf16, int64_t M, int64_t H,
                           uint32_t flags, hipStream_t stream);
+
+/*
+ * A1+A2 with a choice of GeLU form ([LESSON] section 1 names GeLU, [GELU]
+ * gives both forms):  Y_i = act(X . W1[:, C_i] + b1[C_i]).
+ * Arguments, layouts and validation as tp_colpar_gelu, plus
+ *   act not TP_GELU_TANH or TP_GELU_ERF                  -> TP_ERR_UNSUPPORTED
+ * act = TP_GELU_TANH gives exactly tp_colpar_gelu's result.
+ */
+tp_status tp_colpar_act(const void *X, const void *W1t, const void *b1, void *Y_i, int64_t M,
+                        int64_t H, int64_t F, int32_t T, int32_t i, tp_act act, tp_dtype dt,
+                        hipStream_t stream);
+
+/*
+ * Gated first layer, rank i ([SLICE] "Column-Parallel & Row-Parallel GEMMs"
+ * names the first linear layer "Gate/Up" and splits it by columns): a gate
+ * and an up projection of width F, both split into the same column blocks,
+ * combined elementwise, so no communication follows:
+ *   Y_i = act(X . Wg[:, C_i] + bg[C_i]) * (X . Wu[:, C_i] + bu[C_i])
+ *   Wg_t, Wu_t  Wg^T, Wu^T, each [F][H] K-contiguous like W1t
+ *   bg, bu      [F] each, or NULL (no bias)
+ *   Y_i         [M][Fs], input dtype; feeds tp_rowpar_partial like GeLU's Y_i
+ * Validation as tp_colpar_gelu for X, Wg_t, bg, Y_i, plus Wu_t non-NULL
+ * (TP_ERR_NULL), act known, Wu_t and bu 16-byte aligned (TP_ERR_UNSUPPORTED),
+ * Y_i overlapping Wu_t or bu (TP_ERR_ALIAS).
+ */
+tp_status tp_colpar_gated(const void *X, const void *Wg_t, const void *Wu_t, const void *bg,
+                          const void *bu, void *Y_i, int64_t M, int64_t H, int64_t F, int32_t T,
+                          int32_t i, tp_act act, tp_dtype dt, hipStream_t stream);
 
 /*
  * Rank i's whole MLP share ([LESSON] section 1 pipeline: input, column-

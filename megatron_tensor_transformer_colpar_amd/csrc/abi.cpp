@@ -133,8 +133,8 @@ void rowpar_entry(tpk::GemmArgs &g, int b, const void *Y_i, const void *W2t, flo
     g.C[b] = Z_i;
 }
 
-tp_status run_colpar(const void *X, const void *W1t, const void *b1, void *const *Y, int nshard, int32_t i0,
-                     int64_t M, int64_t H, int64_t F, int32_t T, tp_dtype dt, hipStream_t s)
+tpk::GemmArgs colpar_args(const void *X, const void *W1t, const void *b1, void *const *Y, int nshard, int32_t i0,
+                          int64_t M, int64_t H, int64_t F, int32_t T, tp_dtype dt)
 {
     const int64_t Fs = F / T;
     tpk::GemmArgs g = empty_args();
@@ -146,7 +146,14 @@ tp_status run_colpar(const void *X, const void *W1t, const void *b1, void *const
     g.M = M;
     g.N = Fs;
     g.K = H;
-    const hipError_t e = launch(g, tpk::EPI_BIAS_GELU, dt, s);
+    return g;
+}
+
+tp_status run_colpar(const void *X, const void *W1t, const void *b1, void *const *Y, int nshard, int32_t i0,
+                     int64_t M, int64_t H, int64_t F, int32_t T, tp_dtype dt, hipStream_t s,
+                     tpk::Epilogue epi = tpk::EPI_BIAS_GELU)
+{
+    const hipError_t e = launch(colpar_args(X, W1t, b1, Y, nshard, i0, M, H, F, T, dt), epi, dt, s);
     return e == hipSuccess ? ok() : hip_fail(e, "column-parallel launch");
 }
 
@@ -200,6 +207,33 @@ tp_status validate_rowpar(const char *fn, const void *Y_i, const void *W2t, cons
     return TP_OK;
 }
 
+tp_status check_act(const char *fn, tp_act act)
+{
+    if (act != TP_GELU_TANH && act != TP_GELU_ERF)
+        return fail(TP_ERR_UNSUPPORTED, "%s: unknown activation %d", fn, (int)act);
+    return TP_OK;
+}
+
+// The gated first layer: the gate operands are checked as the plain
+// column-parallel call's, then the up weights and bias.
+tp_status validate_gated(const char *fn, const void *X, const void *Wgt, const void *Wut, const void *bg,
+                         const void *bu, const void *Y_i, int64_t M, int64_t H, int64_t F, int32_t T, int32_t i,
+                         tp_act act, tp_dtype dt)
+{
+    tp_status st = check_shard(fn, M, H, F, T, i, dt);
+    if (st != TP_OK) return st;
+    if (!Wut) return fail(TP_ERR_NULL, "%s: X, Wg_t, Wu_t and Y_i must be non-NULL", fn);
+    if ((st = validate_colpar(fn, X, Wgt, bg, Y_i, M, H, F, T, i, dt)) != TP_OK) return st;
+    if ((st = check_act(fn, act)) != TP_OK) return st;
+    if (!aligned16(Wut) || (bu && !aligned16(bu)))
+        return fail(TP_ERR_UNSUPPORTED, "%s: Wu_t and bu must be 16-byte aligned", fn);
+    const int es = element_size(dt);
+    const Range y = span(Y_i, M * (F / T) * es);
+    if (M > 0 && (overlap(y, span(Wut, F * H * es)) || (bu && overlap(y, span(bu, F * es)))))
+        return fail(TP_ERR_ALIAS, "%s: Y_i overlaps an input", fn);
+    return TP_OK;
+}
+
 // Validation of the whole-group calls.  X/W1t (column-parallel inputs) and
 // W2t (row-parallel input) may each be absent (nullptr) when the call does
 // not read them; Y_ws is an output of the column-parallel step and an input
@@ -250,6 +284,35 @@ tp_status tp_colpar_gelu(const void *X, const void *W1t, const void *b1, void *Y
     if (st != TP_OK) return st;
     if (M == 0) return ok();
     return run_colpar(X, W1t, b1, &Y_i, 1, i, M, H, F, T, dt, stream);
+}
+
+tp_status tp_colpar_act(const void *X, const void *W1t, const void *b1, void *Y_i, int64_t M, int64_t H,
+                        int64_t F, int32_t T, int32_t i, tp_act act, tp_dtype dt, hipStream_t stream)
+{
+    const char *fn = "tp_colpar_act";
+    tp_status st = validate_colpar(fn, X, W1t, b1, Y_i, M, H, F, T, i, dt);
+    if (st != TP_OK) return st;
+    if ((st = check_act(fn, act)) != TP_OK) return st;
+    if (M == 0) return ok();
+    return run_colpar(X, W1t, b1, &Y_i, 1, i, M, H, F, T, dt, stream,
+                      act == TP_GELU_ERF ? tpk::EPI_BIAS_GELU_ERF : tpk::EPI_BIAS_GELU);
+}
+
+tp_status tp_colpar_gated(const void *X, const void *Wgt, const void *Wut, const void *bg, const void *bu,
+                          void *Y_i, int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, tp_act act,
+                          tp_dtype dt, hipStream_t stream)
+{
+    const tp_status st =
+        validate_gated("tp_colpar_gated", X, Wgt, Wut, bg, bu, Y_i, M, H, F, T, i, act, dt);
+    if (st != TP_OK) return st;
+    if (M == 0) return ok();
+    const int64_t Fs = F / T;
+    const int es = element_size(dt);
+    tpk::GemmArgs g = colpar_args(X, Wgt, bg, &Y_i, 1, i, M, H, F, T, dt);
+    g.B2[0] = static_cast<const char *>(Wut) + (int64_t)i * Fs * H * es;
+    g.bias2[0] = bu ? static_cast<const char *>(bu) + (int64_t)i * Fs * es : nullptr;
+    const hipError_t e = launch(g, act == TP_GELU_ERF ? tpk::EPI_GATED_ERF : tpk::EPI_GATED_TANH, dt, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "gated column-parallel launch");
 }
 
 tp_status tp_rowpar_partial(const void *Y_i, const void *W2t, float *Z_i, int64_t M, int64_t H, int64_t F,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tp_kernels.h"
+
 namespace tpk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -37,6 +39,23 @@ __device__ __forceinline__ float gelu_tanh(float x)
     const float two_k = 1.5957691216057308f;  // 2 * sqrt(2/pi)
     const float v = two_k * x * (1.0f + 0.044715f * x * x);
     return __fdividef(x, 1.0f + __expf(-v));
+}
+
+// GeLU, exact form (Hendrycks & Gimpel): g(x) = x * Phi(x)
+//   = x/2 * (1 + erf(x / sqrt 2)), erf from the device library.
+__device__ __forceinline__ float gelu_erf(float x)
+{
+    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
+
+// The activation an epilogue applies.
+template <int EPI>
+__device__ __forceinline__ float act(float x)
+{
+    if constexpr (EPI == EPI_BIAS_GELU_ERF || EPI == EPI_GATED_ERF)
+        return gelu_erf(x);
+    else
+        return gelu_tanh(x);
 }
 
 // Workgroup id -> (batch entry, tile_m, tile_n).  Consecutive workgroup ids

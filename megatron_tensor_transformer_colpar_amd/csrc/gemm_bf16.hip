@@ -35,6 +35,8 @@ struct GemmDev {
     const __bf16 *A[kMaxBatch];
     const __bf16 *B[kMaxBatch];
     const __bf16 *bias[kMaxBatch];
+    const __bf16 *B2[kMaxBatch];     // gated epilogues: up rows
+    const __bf16 *bias2[kMaxBatch];  // gated epilogues: up bias
     void *C[kMaxBatch];
     int64_t lda, ldb, ldc;
     int M, N, K;
@@ -83,6 +85,13 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 {
     using C_ = Cfg<BM, BN, BK, S, NW>;
     constexpr int TM = C_::TM, TN = C_::TN, STAGE = C_::STAGE, CH = C_::CH, RB = C_::RB, KQ = C_::KQ;
+    // Gated: each wave's WTN rows of the B tile are WTN/2 gate rows followed
+    // by the matching WTN/2 up rows, so accumulator tiles j and j + TN/2 of a
+    // lane hold gate and up of the same output elements; a tile then covers
+    // BN/2 output columns.
+    constexpr bool GATED = epi_gated(EPI);
+    static_assert(!GATED || TN % 2 == 0, "gated tiles pair accumulator tiles within a wave");
+    constexpr int BNO = GATED ? BN / 2 : BN;   // output columns per tile
     __shared__ u32x4 st0[STAGE];
     __shared__ u32x4 st1[STAGE];
     __shared__ u32x4 st2[S > 2 ? STAGE : 1];
@@ -97,17 +106,21 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 
     int bt, tile_m, tile_n;
     map_tile<8>(blockIdx.x, g.batch, g.tiles_m, g.tiles_n, bt, tile_m, tile_n);
-    const int m0 = tile_m * BM, n0 = tile_n * BN;
+    const int m0 = tile_m * BM, n0 = tile_n * BNO;
     const __bf16 *const Abase = g.A[bt];
     const __bf16 *const Bbase = g.B[bt];
     const __bf16 *const bias_p = g.bias[bt];
     void *const Cbase = g.C[bt];
 
-    const int a_rows = min(BM, g.M - m0), b_rows = min(BN, g.N - n0);
+    const int a_rows = min(BM, g.M - m0), b_rows = min(BNO, g.N - n0);
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(Abase + (int64_t)m0 * g.lda, (uint32_t)((int64_t)a_rows * g.lda * 2));
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(Bbase + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * 2));
+    // (resources are only ever built from pointers: a conditional expression
+    // of resource type makes the host compilation drop the kernel's stub)
+    const __amdgpu_buffer_rsrc_t rb2 =
+        make_rsrc((GATED ? g.B2[bt] : Bbase) + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * 2));
 
     // DMA geometry: instruction j of wave w fills 1 KiB block (NW*j + w),
     // i.e. rows RB(NW*j + w) .. +RB-1; lane L lands in slot L of the block
@@ -120,6 +133,18 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     const uint32_t b_voff = (uint32_t)(drow * g.ldb * 2 + dchunk * 16);
     const uint32_t a_jstep = (uint32_t)(NW * RB * g.lda * 2), b_jstep = (uint32_t)(NW * RB * g.ldb * 2);
     const int KT = g.K / BK;
+    // Gated B rows: instruction j of this wave fills tile rows r0 .. r0+RB-1,
+    // r0 = RB(NW*j + wave), all in one half of one wave's WTN rows; they come
+    // from output rows ob .. ob+RB-1 of the gate (first half) or up matrix.
+    uint32_t gv_off[C_::B_LD];
+    bool gv_up[C_::B_LD];
+#pragma unroll
+    for (int j = 0; j < C_::B_LD; ++j) {
+        const int r0 = RB * (NW * j + wave), rr = r0 % C_::WTN;
+        gv_up[j] = rr >= C_::WTN / 2;
+        const int ob = (r0 / C_::WTN) * (C_::WTN / 2) + rr % (C_::WTN / 2);
+        gv_off[j] = (uint32_t)((ob + lane / CH) * g.ldb * 2 + dchunk * 16);
+    }
 
     // The row offset stays in the per-lane voffset, which the buffer range
     // check covers, so rows past M or N read zero; the in-row K offset goes
@@ -131,9 +156,21 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(stage + (NW * j + wave) * 64), 16,
                                                     a_voff + j * a_jstep, koff, 0, 0);
 #pragma unroll
-        for (int j = 0; j < C_::B_LD; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16,
-                                                    b_voff + j * b_jstep, koff, 0, 0);
+        for (int j = 0; j < C_::B_LD; ++j) {
+            if constexpr (GATED) {
+                // the offset goes through a local: an array element passed
+                // straight to the builtin also makes the host pass drop the stub
+                const uint32_t vo = gv_off[j];
+                if (gv_up[j])
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb2, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16,
+                                                            vo, koff, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16,
+                                                            vo, koff, 0, 0);
+            } else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16,
+                                                        b_voff + j * b_jstep, koff, 0, 0);
+        }
     };
 
     // fragment geometry: lane reads row (lane & 31) of each 32-row tile,
@@ -249,43 +286,77 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     //   m = tile row base + lane%32,  n = tile column base + 8*(v/4) + 4*(lane/32) + v%4,
     // so each lane owns runs of 4 consecutive columns: one 16-byte fp32
     // store or one 8-byte bf16 store per run.
-    const bool full = (m0 + BM <= g.M) && (n0 + BN <= g.N);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int nb = n0 + wn * C_::WTN + j * 32 + 4 * fhalf;
-        f32x4 bias[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bias[q] = f32x4{};
-            if (EPI == EPI_BIAS_GELU && bias_p && (full || nb + 8 * q < g.N)) {
-                const bf16x4 b4 = *reinterpret_cast<const bf16x4 *>(bias_p + nb + 8 * q);
-                bias[q] = f32x4{(float)b4[0], (float)b4[1], (float)b4[2], (float)b4[3]};
-            }
+    const bool full = (m0 + BM <= g.M) && (n0 + BNO <= g.N);
+    auto load_bias = [&](const __bf16 *bp, int nb, int q) __attribute__((always_inline)) {
+        f32x4 v = f32x4{};
+        if (bp && (full || nb + 8 * q < g.N)) {
+            const bf16x4 b4 = *reinterpret_cast<const bf16x4 *>(bp + nb + 8 * q);
+            v = f32x4{(float)b4[0], (float)b4[1], (float)b4[2], (float)b4[3]};
         }
+        return v;
+    };
+    if constexpr (GATED) {
+        const __bf16 *const bias2_p = g.bias2[bt];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int m = m0 + wm * C_::WTM + i * 32 + frow;
-            if (!full && m >= g.M) continue;
+        for (int j = 0; j < TN / 2; ++j) {
+            const int nb = n0 + wn * (C_::WTN / 2) + j * 32 + 4 * fhalf;
+            f32x4 bg[4], bu[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int n = nb + 8 * q;
-                if (!full && n >= g.N) continue;
-                f32x4 x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                if (EPI == EPI_BIAS_GELU) {
-                    x += bias[q];
-                    const bf16x4 y = {(__bf16)gelu_tanh(x[0]), (__bf16)gelu_tanh(x[1]), (__bf16)gelu_tanh(x[2]),
-                                      (__bf16)gelu_tanh(x[3])};
+                bg[q] = load_bias(bias_p, nb, q);
+                bu[q] = load_bias(bias2_p, nb, q);
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int m = m0 + wm * C_::WTM + i * 32 + frow;
+                if (!full && m >= g.M) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = nb + 8 * q;
+                    if (!full && n >= g.N) continue;
+                    const f32x4 ga = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                           acc[i][j][4 * q + 3]} + bg[q];
+                    const int ju = j + TN / 2;
+                    const f32x4 up = f32x4{acc[i][ju][4 * q], acc[i][ju][4 * q + 1], acc[i][ju][4 * q + 2],
+                                           acc[i][ju][4 * q + 3]} + bu[q];
+                    const bf16x4 y = {(__bf16)(act<EPI>(ga[0]) * up[0]), (__bf16)(act<EPI>(ga[1]) * up[1]),
+                                      (__bf16)(act<EPI>(ga[2]) * up[2]), (__bf16)(act<EPI>(ga[3]) * up[3])};
                     *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * g.ldc + n) = y;
-                } else {
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * g.ldc + n) = x;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int nb = n0 + wn * C_::WTN + j * 32 + 4 * fhalf;
+            f32x4 bias[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bias[q] = EPI == EPI_STORE_F32 ? f32x4{} : load_bias(bias_p, nb, q);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int m = m0 + wm * C_::WTM + i * 32 + frow;
+                if (!full && m >= g.M) continue;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = nb + 8 * q;
+                    if (!full && n >= g.N) continue;
+                    f32x4 x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    if (EPI == EPI_STORE_F32) {
+                        *reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * g.ldc + n) = x;
+                    } else {
+                        x += bias[q];
+                        const bf16x4 y = {(__bf16)act<EPI>(x[0]), (__bf16)act<EPI>(x[1]), (__bf16)act<EPI>(x[2]),
+                                          (__bf16)act<EPI>(x[3])};
+                        *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * g.ldc + n) = y;
+                    }
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, int BK, int S, int NW, bool IL>
-hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
+template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI>
+hipError_t launch_one(const GemmArgs &a, hipStream_t s)
 {
     GemmDev g;
     for (int b = 0; b < kMaxBatch; ++b) {
@@ -293,6 +364,8 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
         g.A[b] = static_cast<const __bf16 *>(a.A[src]);
         g.B[b] = static_cast<const __bf16 *>(a.B[src]);
         g.bias[b] = static_cast<const __bf16 *>(a.bias[src]);
+        g.B2[b] = static_cast<const __bf16 *>(a.B2[src]);
+        g.bias2[b] = static_cast<const __bf16 *>(a.bias2[src]);
         g.C[b] = a.C[src];
     }
     g.lda = a.lda;
@@ -302,14 +375,30 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
     g.N = (int)a.N;
     g.K = (int)a.K;
     g.batch = a.batch;
+    constexpr int BNO = epi_gated(EPI) ? BN / 2 : BN;
     g.tiles_m = (int)((a.M + BM - 1) / BM);
-    g.tiles_n = (int)((a.N + BN - 1) / BN);
+    g.tiles_n = (int)((a.N + BNO - 1) / BNO);
     const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(NW * 64);
-    if (epi == EPI_BIAS_GELU)
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU>), grid, block, 0, s, g);
-    else
-        hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI_STORE_F32>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI>), grid, block, 0, s, g);
     return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int S, int NW, bool IL>
+hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
+{
+    constexpr bool gated_ok = Cfg<BM, BN, BK, S, NW>::TN % 2 == 0;
+    switch (epi) {
+    case EPI_BIAS_GELU: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU>(a, s);
+    case EPI_STORE_F32: return launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32>(a, s);
+    case EPI_BIAS_GELU_ERF: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU_ERF>(a, s);
+    case EPI_GATED_TANH:
+        if constexpr (gated_ok) return launch_one<BM, BN, BK, S, NW, IL, EPI_GATED_TANH>(a, s);
+        break;
+    case EPI_GATED_ERF:
+        if constexpr (gated_ok) return launch_one<BM, BN, BK, S, NW, IL, EPI_GATED_ERF>(a, s);
+        break;
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -332,6 +421,12 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, Epilogue epi, int num_cu, hipStre
 #ifndef TP_GEMM_SMALL
 #define TP_GEMM_SMALL 128, 128, 64, 3, 4
 #endif
+    if (epi_gated(epi)) {
+        // a gated tile writes half its width; the 256x128 shape has a single
+        // 32-column accumulator tile per wave and cannot pair gate with up
+        if (tiles(256, 128) >= num_cu) return launch_cfg<TP_GEMM_BIG, TP_GEMM_IL>(a, epi, s);
+        return launch_cfg<TP_GEMM_SMALL, TP_GEMM_IL>(a, epi, s);
+    }
     if (tiles(256, 256) >= num_cu) return launch_cfg<TP_GEMM_BIG, TP_GEMM_IL>(a, epi, s);
     if (tiles(256, 128) >= num_cu) return launch_cfg<TP_GEMM_MID, TP_GEMM_IL>(a, epi, s);
     return launch_cfg<TP_GEMM_SMALL, TP_GEMM_IL>(a, epi, s);

@@ -27,6 +27,8 @@ struct GemvDev {
     const __bf16 *X[kMaxBatch];
     const __bf16 *W[kMaxBatch];
     const __bf16 *bias[kMaxBatch];
+    const __bf16 *W2[kMaxBatch];     // gated epilogues: up rows
+    const __bf16 *bias2[kMaxBatch];  // gated epilogues: up bias
     void *C[kMaxBatch];
     int64_t ldx, ldw, ldc;
     int M, N, K;
@@ -36,27 +38,72 @@ struct GemvDev {
 // so the reused token rows stay resident in L2.
 constexpr int kStreamPolicy = 2;
 
+// Output element idx (< MT*256) of a block, from the KS partial tiles in
+// LDS summed in fixed order.  Accumulator element v of lane l, token tile mt
+// is weight row 4*(l/16) + v, token mt*16 + l%16.  Plain blocks are 16
+// output columns from n0; gated blocks are 8 gate rows then the 8 matching
+// up rows, i.e. 8 output columns from n0, and only lanes l < 32 (rows 0..7)
+// write, pairing with the up sum at idx + 32 (row + 8).
+template <int EPI, int MT, int KS>
+__device__ __forceinline__ void gemv_store(const GemvDev &g, int bt, int n0, int idx, const float (*red)[MT * 4 * 64])
+{
+    const int l = idx & 63, v = (idx >> 6) & 3, mt = idx >> 8;
+    const int m = mt * 16 + (l & 15);
+    if (m >= g.M) return;
+    auto sum = [&](int k) __attribute__((always_inline)) {
+        float s = red[0][k];
+#pragma unroll
+        for (int j = 1; j < KS; ++j) s += red[j][k];
+        return s;
+    };
+    if constexpr (epi_gated(EPI)) {
+        if (l >= 32) return;
+        const int n = n0 + 4 * (l >> 4) + v;
+        const float bg = g.bias[bt] ? (float)g.bias[bt][n] : 0.0f;
+        const float bu = g.bias2[bt] ? (float)g.bias2[bt][n] : 0.0f;
+        const float y = act<EPI>(sum(idx) + bg) * (sum(idx + 32) + bu);
+        static_cast<__bf16 *>(g.C[bt])[(int64_t)m * g.ldc + n] = (__bf16)y;
+    } else {
+        const int n = n0 + 4 * (l >> 4) + v;
+        const float s = sum(idx);
+        if (EPI == EPI_STORE_F32) {
+            static_cast<float *>(g.C[bt])[(int64_t)m * g.ldc + n] = s;
+        } else {
+            const float b = g.bias[bt] ? (float)g.bias[bt][n] : 0.0f;
+            static_cast<__bf16 *>(g.C[bt])[(int64_t)m * g.ldc + n] = (__bf16)act<EPI>(s + b);
+        }
+    }
+}
+
 template <int EPI, int MT, int KS, int CHUNK>
 __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
 {
     __shared__ float red[KS][MT * 4 * 64];
 
+    constexpr bool GATED = epi_gated(EPI);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * (GATED ? 8 : 16);   // first output column
     const int bt = blockIdx.y;   // batch entry (TP shard)
     const __bf16 *const Xb = g.X[bt];
     const __bf16 *const Wb = g.W[bt];
     const int Kw = g.K / KS;
     const int kbeg = w * Kw;
 
+    // gated: rows 0..7 of the block are gate rows, 8..15 the up rows
     const __amdgpu_buffer_rsrc_t wsrc =
-        make_rsrc(Wb + (int64_t)n0 * g.ldw, (uint32_t)(16 * g.ldw * 2));
+        make_rsrc(Wb + (int64_t)n0 * g.ldw, (uint32_t)((GATED ? 8 : 16) * g.ldw * 2));
+    const __amdgpu_buffer_rsrc_t wsrc2 = make_rsrc((GATED ? g.W2[bt] : Wb) + (int64_t)n0 * g.ldw,
+                                                   (uint32_t)((GATED ? 8 : 16) * g.ldw * 2));
     const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(Xb, (uint32_t)((int64_t)g.M * g.ldx * 2));
 
     // lane geometry of the 16x16x32 MFMA operands: row (lane & 15), K chunk
     // (lane >> 4) of 8 elements
     const int r16 = lane & 15, kq = (lane >> 4) * 8;
     const uint32_t w_voff = (uint32_t)((r16 * g.ldw + kbeg + kq) * 2);
+    // gated: a gate lane's offset in the up matrix, and an up lane's in the
+    // gate matrix, lie past the 8-row range and read zero (and no memory),
+    // so the OR of the two loads is the lane's own row
+    const uint32_t w_voff2 = (uint32_t)(((r16 - 8) * g.ldw + kbeg + kq) * 2);
     uint32_t x_voff[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) x_voff[mt] = (uint32_t)(((mt * 16 + r16) * g.ldx + kbeg + kq) * 2);
@@ -72,8 +119,12 @@ __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
         u32x4 wv[CHUNK], xv[CHUNK][MT];
         const uint32_t soff = (uint32_t)k * 2;
 #pragma unroll
-        for (int c = 0; c < CHUNK; ++c)
+        for (int c = 0; c < CHUNK; ++c) {
             wv[c] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, (int)(w_voff + c * 64), (int)soff, kStreamPolicy);
+            if constexpr (GATED)
+                wv[c] |= __builtin_amdgcn_raw_buffer_load_b128(wsrc2, (int)(w_voff2 + c * 64), (int)soff,
+                                                               kStreamPolicy);
+        }
 #pragma unroll
         for (int c = 0; c < CHUNK; ++c)
 #pragma unroll
@@ -99,21 +150,7 @@ __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
         for (int v = 0; v < 4; ++v) red[w][(mt * 4 + v) * 64 + lane] = acc[mt][v];
     __syncthreads();
 
-    for (int idx = t; idx < MT * 4 * 64; idx += KS * 64) {
-        float s = red[0][idx];
-#pragma unroll
-        for (int j = 1; j < KS; ++j) s += red[j][idx];
-        const int l = idx & 63, v = (idx >> 6) & 3, mt = idx >> 8;
-        const int m = mt * 16 + (l & 15);
-        const int n = n0 + 4 * (l >> 4) + v;
-        if (m >= g.M) continue;
-        if (EPI == EPI_BIAS_GELU) {
-            const float b = g.bias[bt] ? (float)g.bias[bt][n] : 0.0f;
-            static_cast<__bf16 *>(g.C[bt])[(int64_t)m * g.ldc + n] = (__bf16)gelu_tanh(s + b);
-        } else {
-            static_cast<float *>(g.C[bt])[(int64_t)m * g.ldc + n] = s;
-        }
-    }
+    for (int idx = t; idx < MT * 4 * 64; idx += KS * 64) gemv_store<EPI, MT, KS>(g, bt, n0, idx, red);
 }
 
 // Segmented stream (used whenever a wave's K range is a multiple of 128):
@@ -134,15 +171,20 @@ __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
     __shared__ u32x4 ulds[KS][256];
     __shared__ float red[KS][MT * 4 * 64];
 
+    constexpr bool GATED = epi_gated(EPI);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * (GATED ? 8 : 16);   // first output column
     const int bt = blockIdx.y;
     const int Kw = g.K / KS;
     const int kbeg = w * Kw;
     const int units = Kw / 128;
 
+    // gated: instructions 0, 1 read gate rows 0..7, instructions 2, 3 the
+    // matching up rows, which become rows 8..15 of the block
     const __amdgpu_buffer_rsrc_t wsrc =
-        make_rsrc(g.W[bt] + (int64_t)n0 * g.ldw, (uint32_t)(16 * g.ldw * 2));
+        make_rsrc(g.W[bt] + (int64_t)n0 * g.ldw, (uint32_t)((GATED ? 8 : 16) * g.ldw * 2));
+    const __amdgpu_buffer_rsrc_t wsrc2 = make_rsrc((GATED ? g.W2[bt] : g.W[bt]) + (int64_t)n0 * g.ldw,
+                                                   (uint32_t)((GATED ? 8 : 16) * g.ldw * 2));
     const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(g.X[bt], (uint32_t)((int64_t)g.M * g.ldx * 2));
 
     const int a = lane >> 4, b = lane & 15;
@@ -150,7 +192,7 @@ __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
     int wslot[4], rslot[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        w_voff[i] = (uint32_t)(((4 * i + a) * g.ldw + kbeg) * 2 + b * 16);
+        w_voff[i] = (uint32_t)(((4 * (GATED ? (i & 1) : i) + a) * g.ldw + kbeg) * 2 + b * 16);
         wslot[i] = i * 64 + a * 16 + (b ^ (4 * i + a));
         rslot[i] = (b >> 2) * 64 + (b & 3) * 16 + ((4 * i + a) ^ b);
     }
@@ -166,7 +208,12 @@ __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
     auto issue = [&](int u, int d) __attribute__((always_inline)) {
         const int so = u * 256;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wv[d][i] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, (int)w_voff[i], so, kStreamPolicy);
+        for (int i = 0; i < 4; ++i) {
+            if (GATED && i >= 2)
+                wv[d][i] = __builtin_amdgcn_raw_buffer_load_b128(wsrc2, (int)w_voff[i], so, kStreamPolicy);
+            else
+                wv[d][i] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, (int)w_voff[i], so, kStreamPolicy);
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -202,29 +249,13 @@ __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
         for (int v = 0; v < 4; ++v) red[w][(mt * 4 + v) * 64 + lane] = acc[mt][v];
     __syncthreads();
 
-    void *const Cb = g.C[bt];
-    const __bf16 *const bias = g.bias[bt];
-    for (int idx = t; idx < MT * 4 * 64; idx += KS * 64) {
-        float s = red[0][idx];
-#pragma unroll
-        for (int j = 1; j < KS; ++j) s += red[j][idx];
-        const int l = idx & 63, v = (idx >> 6) & 3, mt = idx >> 8;
-        const int m = mt * 16 + (l & 15);
-        const int n = n0 + 4 * (l >> 4) + v;
-        if (m >= g.M) continue;
-        if (EPI == EPI_BIAS_GELU) {
-            const float bb = bias ? (float)bias[n] : 0.0f;
-            static_cast<__bf16 *>(Cb)[(int64_t)m * g.ldc + n] = (__bf16)gelu_tanh(s + bb);
-        } else {
-            static_cast<float *>(Cb)[(int64_t)m * g.ldc + n] = s;
-        }
-    }
+    for (int idx = t; idx < MT * 4 * 64; idx += KS * 64) gemv_store<EPI, MT, KS>(g, bt, n0, idx, red);
 }
 
 template <int EPI, int MT, int KS>
 hipError_t launch_ks(const GemvDev &g, int batch, hipStream_t s)
 {
-    const dim3 grid((unsigned)(g.N / 16), (unsigned)batch);
+    const dim3 grid((unsigned)(g.N / (epi_gated(EPI) ? 8 : 16)), (unsigned)batch);
     if ((g.K / KS) % 128 == 0) {
         hipLaunchKernelGGL((gemv_seg_kernel<EPI, MT, KS, 2>), grid, dim3(KS * 64), 0, s, g);
         return hipGetLastError();
@@ -259,6 +290,8 @@ hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int /*num_cu*/, hip
         g.X[b] = static_cast<const __bf16 *>(a.A[src]);
         g.W[b] = static_cast<const __bf16 *>(a.B[src]);
         g.bias[b] = static_cast<const __bf16 *>(a.bias[src]);
+        g.W2[b] = static_cast<const __bf16 *>(a.B2[src]);
+        g.bias2[b] = static_cast<const __bf16 *>(a.bias2[src]);
         g.C[b] = a.C[src];
     }
     g.ldx = a.lda;
@@ -268,9 +301,19 @@ hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int /*num_cu*/, hip
     g.N = (int)a.N;
     g.K = (int)a.K;
     const bool two = a.M > 16;
-    if (epi == EPI_BIAS_GELU)
+    switch (epi) {
+    case EPI_BIAS_GELU:
         return two ? launch_mt<EPI_BIAS_GELU, 2>(g, a.batch, s) : launch_mt<EPI_BIAS_GELU, 1>(g, a.batch, s);
-    return two ? launch_mt<EPI_STORE_F32, 2>(g, a.batch, s) : launch_mt<EPI_STORE_F32, 1>(g, a.batch, s);
+    case EPI_STORE_F32:
+        return two ? launch_mt<EPI_STORE_F32, 2>(g, a.batch, s) : launch_mt<EPI_STORE_F32, 1>(g, a.batch, s);
+    case EPI_BIAS_GELU_ERF:
+        return two ? launch_mt<EPI_BIAS_GELU_ERF, 2>(g, a.batch, s) : launch_mt<EPI_BIAS_GELU_ERF, 1>(g, a.batch, s);
+    case EPI_GATED_TANH:
+        return two ? launch_mt<EPI_GATED_TANH, 2>(g, a.batch, s) : launch_mt<EPI_GATED_TANH, 1>(g, a.batch, s);
+    case EPI_GATED_ERF:
+        return two ? launch_mt<EPI_GATED_ERF, 2>(g, a.batch, s) : launch_mt<EPI_GATED_ERF, 1>(g, a.batch, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace tpk

@@ -10,22 +10,30 @@ namespace tpk {
 
 // What a GEMM does with its fp32 accumulator tile.
 enum Epilogue : int {
-    EPI_BIAS_GELU = 0,  // + bias[n] (if any), GeLU(tanh), store in the input dtype
-    EPI_STORE_F32 = 1,  // store the fp32 accumulator (row-parallel partial)
+    EPI_BIAS_GELU = 0,      // + bias[n] (if any), GeLU (tanh form), store in the input dtype
+    EPI_STORE_F32 = 1,      // store the fp32 accumulator (row-parallel partial)
+    EPI_BIAS_GELU_ERF = 2,  // + bias[n] (if any), GeLU (exact x*Phi(x)), input dtype
+    EPI_GATED_TANH = 3,     // GeLU_tanh(gate + bias[n]) * (up + bias2[n]), input dtype
+    EPI_GATED_ERF = 4,      // GeLU_erf(gate + bias[n]) * (up + bias2[n]), input dtype
 };
+constexpr bool epi_gated(int e) { return e == EPI_GATED_TANH || e == EPI_GATED_ERF; }
 
 // C[m][n] = sum_k A[m][k] * B[n][k]  (both operands K-contiguous), then the
 // epilogue.  A: M rows, stride lda; B: N rows, stride ldb; C: stride ldc.
 // `batch` independent problems of the same shape (one per TP shard when the
 // whole TP group is emulated on one GPU) may be launched together; entry b
-// of each pointer array belongs to problem b.
+// of each pointer array belongs to problem b.  The gated epilogues take a
+// second weight matrix B2 (the up rows; B holds the gate rows, same N, K and
+// stride) and a second bias, and write N columns.
 constexpr int kMaxBatch = 8;
 struct GemmArgs {
     const void *A[kMaxBatch];
     int64_t lda;
     const void *B[kMaxBatch];
     int64_t ldb;
-    const void *bias[kMaxBatch];  // [N] or nullptr (EPI_BIAS_GELU only)
+    const void *bias[kMaxBatch];   // [N] or nullptr (activation epilogues)
+    const void *B2[kMaxBatch];     // gated epilogues: up rows, else unused
+    const void *bias2[kMaxBatch];  // gated epilogues: up bias [N] or nullptr
     void *C[kMaxBatch];
     int64_t ldc;
     int64_t M, N, K;

@@ -17,6 +17,7 @@ import numpy as np
 
 # tensor ids for the seed sequence
 X_ID, W1_ID, B1_ID, W2_ID, CTX_ID, WO_ID = 0, 1, 2, 3, 4, 5
+WG_ID, WU_ID, BG_ID, BU_ID = 6, 7, 8, 9   # gated first layer: gate and up weights and biases
 
 
 def f32_to_bf16_bits(x) -> np.ndarray:
@@ -134,6 +135,24 @@ WORKLOADS = {
     "prefill": Workload(4, "prefill", "bf16", M=8192, H=8192, F=32768, T=8),
     "stack80": Workload(5, "stack80", "bf16", M=8, H=8192, F=32768, T=8, A=8192, layers=80),
 }
+
+
+def gated_inputs(w: Workload, *, M: int | None = None, seed: int = 0, layer: int = 0,
+                 shard_only: int | None = None):
+    """X [M,H], Wg [H,F], Wu [H,F], bg [F], bu [F] for the gated first layer,
+    drawn like the plain layer's X, W1 and b1 (same distributions)."""
+    M = w.M if M is None else M
+    kw = dict(seed=seed, workload=w.wid, layer=layer)
+    X = normal((M, w.H), w.x_std, w.dtype, tensor=X_ID, **kw)
+    if shard_only is None:
+        F, sh = w.F, 0
+    else:
+        F, sh = w.F // w.T, shard_only + 1
+    Wg = normal((w.H, F), w.w_std, w.dtype, tensor=WG_ID, shard=sh, **kw)
+    Wu = normal((w.H, F), w.w_std, w.dtype, tensor=WU_ID, shard=sh, **kw)
+    bg = normal((F,), w.b_std, w.dtype, tensor=BG_ID, shard=sh, **kw)
+    bu = normal((F,), w.b_std, w.dtype, tensor=BU_ID, shard=sh, **kw)
+    return X, Wg, Wu, bg, bu
 
 
 def mlp_inputs(w: Workload, *, M: int | None = None, seed: int = 0, layer: int = 0,

@@ -36,6 +36,7 @@ TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_UNSUPPORTED, TP_ERR_HIP, TP_ERR_ALIAS =
 STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_UNSUPPORTED",
                 4: "TP_ERR_HIP", 5: "TP_ERR_ALIAS"}
 TP_BF16, TP_F32 = 0, 1
+TP_GELU_TANH, TP_GELU_ERF = 0, 1
 TP_REDUCE_RMS_BF16 = 1
 TP_RMS_EPS = 1e-6
 TP_MAX_T = 8
@@ -50,8 +51,11 @@ raw.tp_colpar_gelu_group.argtypes = [_vp, _vp, _vp, _pp, _i64, _i64, _i64, _i32,
 raw.tp_rowpar_partial_group.argtypes = [_pp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
 raw.tp_mlp_group_fwd.argtypes = [_vp, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
 raw.tp_layer_fwd.argtypes = [_vp, _vp, _pp, _vp, _i64, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _vp]
+raw.tp_colpar_act.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
+raw.tp_colpar_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
 for _f in (raw.tp_colpar_gelu, raw.tp_rowpar_partial, raw.tp_shard_reduce, raw.tp_mlp_shard_fwd,
-           raw.tp_colpar_gelu_group, raw.tp_rowpar_partial_group, raw.tp_mlp_group_fwd, raw.tp_layer_fwd):
+           raw.tp_colpar_gelu_group, raw.tp_rowpar_partial_group, raw.tp_mlp_group_fwd, raw.tp_layer_fwd,
+           raw.tp_colpar_act, raw.tp_colpar_gated):
     _f.restype = ctypes.c_int
 raw.tp_last_error.argtypes = []
 raw.tp_last_error.restype = ctypes.c_char_p
@@ -60,7 +64,7 @@ raw.tp_version.restype = ctypes.c_char_p
 
 EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_shard_fwd",
            "tp_colpar_gelu_group", "tp_rowpar_partial_group", "tp_mlp_group_fwd", "tp_layer_fwd",
-           "tp_last_error", "tp_version")
+           "tp_colpar_act", "tp_colpar_gated", "tp_last_error", "tp_version")
 
 
 class TPError(RuntimeError):
@@ -139,6 +143,15 @@ def tp_rowpar_partial_group(Y_ws, W2t, Z_parts, M, H, F, T, dt=TP_BF16, stream=N
 def tp_mlp_group_fwd(X, W1t, b1, W2t, Y_ws, Z_parts, M, H, F, T, dt=TP_BF16, stream=None):
     _check(raw.tp_mlp_group_fwd(_ptr(X), _ptr(W1t), _ptr(b1), _ptr(W2t), _arr(Y_ws), _arr(Z_parts), M, H, F, T,
                                 dt, _stream(stream)))
+
+
+def tp_colpar_act(X, W1t, b1, Y_i, M, H, F, T, i, act, dt=TP_BF16, stream=None):
+    _check(raw.tp_colpar_act(_ptr(X), _ptr(W1t), _ptr(b1), _ptr(Y_i), M, H, F, T, i, act, dt, _stream(stream)))
+
+
+def tp_colpar_gated(X, Wgt, Wut, bg, bu, Y_i, M, H, F, T, i, act, dt=TP_BF16, stream=None):
+    _check(raw.tp_colpar_gated(_ptr(X), _ptr(Wgt), _ptr(Wut), _ptr(bg), _ptr(bu), _ptr(Y_i), M, H, F, T, i, act,
+                               dt, _stream(stream)))
 
 
 def tp_layer_fwd(h, xhat, ctx, Wot, A, W1t, b1, W2t, Y_ws, parts, M, H, F, T, stream=None):

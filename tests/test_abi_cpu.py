@@ -223,3 +223,55 @@ def test_layer_rejects(kw, status):
 
 def test_layer_empty_is_ok():
     assert layer(M=0) == tp.TP_OK
+
+
+# ------------------------------------- GeLU form choice and gated first layer
+def colpar_act(X=P[0], W=P[1], b=P[2], Y=P[3], M=4, H=64, F=256, T=4, i=0, act=tp.TP_GELU_ERF, dt=BF16):
+    return tp.raw.tp_colpar_act(X, W, b, Y, M, H, F, T, i, act, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), tp.TP_ERR_SHAPE),
+    (dict(i=4), tp.TP_ERR_SHAPE),
+    (dict(X=None), tp.TP_ERR_NULL),
+    (dict(act=2), tp.TP_ERR_UNSUPPORTED),
+    (dict(act=-1), tp.TP_ERR_UNSUPPORTED),
+    (dict(H=96), tp.TP_ERR_UNSUPPORTED),
+    (dict(Y=P[0] + 64), tp.TP_ERR_ALIAS),
+])
+def test_colpar_act_rejects(kw, status):
+    assert colpar_act(**kw) == status
+    assert "tp_colpar_act" in tp.last_error()
+
+
+def gated(X=P[0], Wg=P[1], Wu=P[4], bg=P[2], bu=P[5], Y=P[3], M=4, H=64, F=256, T=4, i=0,
+          act=tp.TP_GELU_TANH, dt=BF16):
+    return tp.raw.tp_colpar_gated(X, Wg, Wu, bg, bu, Y, M, H, F, T, i, act, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=3), tp.TP_ERR_SHAPE),
+    (dict(i=-1), tp.TP_ERR_SHAPE),
+    (dict(X=None), tp.TP_ERR_NULL),
+    (dict(Wg=None), tp.TP_ERR_NULL),
+    (dict(Wu=None), tp.TP_ERR_NULL),
+    (dict(Y=None), tp.TP_ERR_NULL),
+    (dict(act=5), tp.TP_ERR_UNSUPPORTED),
+    (dict(dt=3), tp.TP_ERR_UNSUPPORTED),
+    (dict(F=4 * 96), tp.TP_ERR_UNSUPPORTED),
+    (dict(Wu=P[4] + 8), tp.TP_ERR_UNSUPPORTED),
+    (dict(bu=P[5] + 2), tp.TP_ERR_UNSUPPORTED),
+    (dict(Y=P[1] + 4096), tp.TP_ERR_ALIAS),      # Y over the gate weights
+    (dict(Y=P[4] + 4096), tp.TP_ERR_ALIAS),      # Y over the up weights
+    (dict(Y=P[5]), tp.TP_ERR_ALIAS),             # Y over the up bias
+])
+def test_colpar_gated_rejects(kw, status):
+    assert gated(**kw) == status
+    assert "tp_colpar_gated" in tp.last_error()
+
+
+def test_variant_empty_calls_are_ok():
+    assert colpar_act(M=0) == tp.TP_OK
+    assert gated(M=0) == tp.TP_OK
+    assert gated(M=0, bg=None, bu=None, act=tp.TP_GELU_ERF) == tp.TP_OK
+    assert tp.last_error() == ""
