@@ -20,6 +20,8 @@ Also reported on the same JSON line:
                 weight sets larger than the last-level cache (HBM GB/s)
   stack80       80 layers (H=8192, F=32768, A=8192, T=8, whole group per
                 layer) at decode M=8 (weight GB/s) and prefill M=4096 (TFLOP/s)
+  variants      rank 0's exact-GeLU and gated Gate/Up first layer: prefill
+                (TFLOP/s) and gated decode at M=8 (weight GB/s)
   hipblaslt_context  the column-parallel launches next to torch.matmul
                 (hipBLASLt) on the same shapes, same GPU, same run
   cpu_baseline  the fp64 oracle on a bounded sample of the headline rows
@@ -209,6 +211,56 @@ def prefill(args, torch, tp):
         mean = sum(d) / len(d)
         out[name + "_tflops"] = round(2.0 * M * H * Fs / (mean * 1e-3) / 1e12, 1)
     log("[bench] prefill: %s" % out)
+    return out
+
+
+def variants(args, torch, tp):
+    """The exact-GeLU and gated Gate/Up first layers of rank 0: prefill at
+    H=8192, F/T=4096, M=8192 (TFLOP/s; gated counts both projections) and the
+    gated decode step at M=8 over rotating weight sets (weight GB/s)."""
+    g = torch.Generator(device="cuda").manual_seed(9)
+    stream = torch.cuda.current_stream().cuda_stream
+    H, Fs = 8192, 4096
+
+    def bf(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+    def timed(f, n):
+        for k in range(3):
+            f(k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(n):
+            f(k)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    out = {}
+    M = 8192
+    X, Wg, Wu, bg, bu = bf(M, H), bf(Fs, H, std=0.02), bf(Fs, H, std=0.02), bf(Fs, std=0.01), bf(Fs, std=0.01)
+    Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+    n = max(3, args.steps // 5)
+    fl = 2.0 * M * H * Fs
+    ms = timed(lambda k: tp.tp_colpar_act(X, Wg, bg, Y, M, H, Fs, 1, 0, tp.TP_GELU_ERF, tp.TP_BF16, stream), n)
+    out["prefill_exact_gelu_tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
+    ms = timed(lambda k: tp.tp_colpar_gated(X, Wg, Wu, bg, bu, Y, M, H, Fs, 1, 0, tp.TP_GELU_TANH, tp.TP_BF16,
+                                            stream), n)
+    out["prefill_gated_tflops"] = round(2 * fl / (ms * 1e-3) / 1e12, 1)
+    del X, Y
+    M, R = 8, args.decode_sets
+    sets = [(bf(Fs, H, std=0.02), bf(Fs, H, std=0.02)) for _ in range(R)]
+    X = bf(M, H)
+    Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+    ms = timed(lambda k: tp.tp_colpar_gated(X, sets[k % R][0], sets[k % R][1], bg, bu, Y, M, H, Fs, 1, 0,
+                                            tp.TP_GELU_TANH, tp.TP_BF16, stream), max(2 * R, args.steps))
+    by = 2.0 * (2 * Fs * H + 2 * Fs) + M * H * 2 + M * Fs * 2
+    out["decode_gated_m8_us"] = round(ms * 1e3, 2)
+    out["decode_gated_m8_gbs"] = round(by / (ms * 1e-3) / 1e9, 1)
+    out["decode_gated_m8_frac"] = round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    out["workload"] = "rank 0 first layer, H=8192 F/T=4096: prefill M=8192, decode M=8"
+    log("[bench] variants: %s" % out)
     return out
 
 
@@ -422,7 +474,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline step only (for profiling)")
-    ap.add_argument("--sections", default="prefill,decode,stack80,context",
+    ap.add_argument("--sections", default="prefill,decode,stack80,variants,context",
                     help="comma-separated extra sections to run after the headline step")
     ap.add_argument("--context-only", action="store_true",
                     help="only the library-vs-hipBLASLt comparison (for counter runs)")
@@ -477,6 +529,8 @@ def main():
     torch.cuda.empty_cache()
     if "stack80" in sections:
         rec["stack80"] = stack80(args, torch, tp)
+    if "variants" in sections:
+        rec["variants"] = variants(args, torch, tp)
     if "context" in sections:
         rec["hipblaslt_context"] = hipblaslt_context(args, torch, tp)
     if not args.no_cpu_baseline:
