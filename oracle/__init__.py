@@ -13,6 +13,9 @@ Sources are cited per function in ``oracle.c``:
     diagram) and section 2 question 2 (GeLU commutes with the column split).
   * "Tensor parallelism" guide, "Concept" and "Walking through a transformer
     block" (column/row parallel, head-sharded attention, residual paths).
+  * Vaswani et al., arXiv:1706.03762, section 3.2 (scaled dot-product and
+    multi-head attention, the decoder's causal mask); Ainslie et al.,
+    arXiv:2305.13245 (grouped key/value heads).
 """
 from __future__ import annotations
 
@@ -54,8 +57,10 @@ def _bind(path):
     lib.orc_rowpar_partial.argtypes = [i64, i64, i64, i32, i32, dp, dp, dp]
     lib.orc_shard_reduce.argtypes = [i32, i64, i64, dp, dp, dp, dp, ctypes.c_double]
     lib.orc_mlp_unsharded.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp]
+    lib.orc_attention.argtypes = [i64, i64, i64, i32, i32, i32, i32, dp, dp, dp, dp, dp]
     for f in (lib.orc_colpar_gelu, lib.orc_rowpar_partial, lib.orc_shard_reduce,
-              lib.orc_mlp_unsharded, lib.orc_act, lib.orc_colpar_act, lib.orc_colpar_gated):
+              lib.orc_mlp_unsharded, lib.orc_act, lib.orc_colpar_act, lib.orc_colpar_gated,
+              lib.orc_attention):
         f.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [i32]
     lib.orc_set_threads.restype = None
@@ -122,12 +127,12 @@ def gelu(x):
     return y
 
 
-ACT_GELU_TANH, ACT_GELU_ERF = 0, 1
+ACT_GELU_TANH, ACT_GELU_ERF, ACT_NONE = 0, 1, 2
 
 
 def act(x, form: int):
     """Either GeLU form elementwise in fp64: ACT_GELU_TANH (tanh approximation)
-    or ACT_GELU_ERF (exact x * Phi(x))."""
+    or ACT_GELU_ERF (exact x * Phi(x)); ACT_NONE is the identity."""
     x = _f64(x)
     y = np.empty_like(x)
     _check(_load().orc_act(int(form), x.size, _p(x), _p(y)), "act")
@@ -148,6 +153,36 @@ def colpar_act(X, W1, b1, T: int, i: int, form: int):
     Y = np.empty((M, F // T))
     _check(_load().orc_colpar_act(M, H, F, T, i, int(form), _p(X), _p(W1), _p(b1), _p(Y)), "colpar_act")
     return Y
+
+
+def colpar_linear(X, W, b, T: int, i: int):
+    """Shard i of T of a column-parallel projection with no activation:
+    X W[:, C_i] + b[C_i] (the attention's query, key and value projections)."""
+    return colpar_act(X, W, b, T, i, ACT_NONE)
+
+
+def attention(Q, K, V, nh: int, nkv: int, causal: bool, kv_len=None):
+    """Scaled dot-product attention of nh query heads over nkv key/value heads.
+
+    Q [Bs, Sq, nh*d], K and V [Bs, Lk, nkv*d]; kv_len: valid keys per sequence
+    (default Lk).  Query s of sequence b sits at position kv_len[b] - Sq + s;
+    causal attention sees keys up to that position.  Returns ctx [Bs, Sq, nh*d].
+    """
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    if Q.ndim != 3 or K.ndim != 3 or K.shape != V.shape or K.shape[0] != Q.shape[0]:
+        raise ValueError("oracle: Q [Bs,Sq,nh*d], K and V [Bs,Lk,nkv*d]")
+    Bs, Sq, qw = Q.shape
+    Lk, kw = K.shape[1], K.shape[2]
+    if qw % nh or kw % nkv or qw // nh != kw // nkv:
+        raise ValueError("oracle: head widths of Q and K/V differ")
+    d = qw // nh
+    lens = None if kv_len is None else np.ascontiguousarray(kv_len, dtype=np.int64)
+    if lens is not None and lens.shape != (Bs,):
+        raise ValueError("oracle: kv_len must have one entry per sequence")
+    ctx = np.empty((Bs, Sq, qw))
+    _check(_load().orc_attention(Bs, Sq, Lk, nh, nkv, d, int(bool(causal)), _p(lens), _p(Q), _p(K), _p(V),
+                                 _p(ctx)), "attention")
+    return ctx
 
 
 def colpar_gated(X, Wg, Wu, bg, bu, T: int, i: int, form: int):

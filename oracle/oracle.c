@@ -30,6 +30,13 @@
  *  [GELU]   Hendrycks & Gimpel, "Gaussian Error Linear Units (GELUs)",
  *           arXiv:1606.08415: the exact form x*Phi(x) and its tanh
  *           approximation.
+ *  [ATTN]   Vaswani et al., "Attention Is All You Need", arXiv:1706.03762:
+ *           section 3.2.1 (scaled dot-product attention), 3.2.2 (multi-head
+ *           attention), 3.2.3 (the decoder masks later positions).
+ *  [GQA]    Ainslie et al., "GQA: Training Generalized Multi-Query
+ *           Transformer Models from Multi-Head Checkpoints",
+ *           arXiv:2305.13245: groups of query heads share one key/value
+ *           head.
  */
 #include <math.h>
 #include <stddef.h>
@@ -59,15 +66,19 @@ static double gelu_erf(double x)
 
 #define ORC_ACT_GELU_TANH 0
 #define ORC_ACT_GELU_ERF 1
+#define ORC_ACT_NONE 2
 
+/* ORC_ACT_NONE is the identity: the column-parallel projection with no
+ * activation (the attention's query, key and value projections). */
 static double act_apply(int32_t act, double x)
 {
+    if (act == ORC_ACT_NONE) return x;
     return act == ORC_ACT_GELU_ERF ? gelu_erf(x) : gelu_tanh(x);
 }
 
 static int act_ok(int32_t act)
 {
-    return act == ORC_ACT_GELU_TANH || act == ORC_ACT_GELU_ERF;
+    return act == ORC_ACT_GELU_TANH || act == ORC_ACT_GELU_ERF || act == ORC_ACT_NONE;
 }
 
 void orc_gelu(int64_t n, const double *x, double *y)
@@ -142,7 +153,8 @@ int orc_colpar_gated(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, int3
                      const double *X, const double *Wg, const double *Wu,
                      const double *bg, const double *bu, double *Y_i)
 {
-    if (!shard_ok(M, H, F, T, i) || !act_ok(act) || !X || !Wg || !Wu || !Y_i) return ORC_BAD_ARG;
+    if (!shard_ok(M, H, F, T, i) || !act_ok(act) || act == ORC_ACT_NONE || !X || !Wg || !Wu || !Y_i)
+        return ORC_BAD_ARG;
     const int64_t Fs = F / T, o = (int64_t)i * Fs;
     #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m) {
@@ -243,6 +255,74 @@ int orc_mlp_unsharded(int64_t M, int64_t H, int64_t F,
     if (rc == ORC_OK) rc = orc_rowpar_partial(M, H, F, 1, 0, y, W2, Z);
     if (!Y) free(y);
     return rc;
+}
+
+/* Scaled dot-product attention of one rank's heads ([ATTN] 3.2.1, 3.2.2;
+ * [GUIDE] "Walking through a transformer block": a rank owns a block of
+ * query heads, or of GQA groups, and the matching key/value heads, so the
+ * same function serves every rank on its own slices).
+ *
+ * Layouts, row-major: Q [Bs][Sq][nh][d], K and V [Bs][Lk][nkv][d],
+ * ctx [Bs][Sq][nh][d].  Sequence b holds len_b = kv_len[b] valid keys
+ * (kv_len NULL: Lk for every sequence); its Sq queries are its last Sq
+ * positions, so query s sits at position p = len_b - Sq + s.  Query head h
+ * reads key/value head h / G, G = nh / nkv ([GQA]: consecutive query heads
+ * form a group).  Causal ([ATTN] 3.2.3, a decoder's self-attention): query
+ * p sees keys t = 0..p; otherwise keys t = 0..len_b-1.
+ *
+ *   s_t   = ( sum_e q[e] k_t[e] ) / sqrt(d)
+ *   w_t   = exp(s_t - max_t s_t) / sum_t exp(s_t - max_t s_t)
+ *   ctx_e = sum_t w_t v_t[e]
+ *
+ * Subtracting the maximum leaves the softmax unchanged and keeps exp finite.
+ * Needs 1 <= len_b <= Lk, and len_b >= Sq when causal. */
+int orc_attention(int64_t Bs, int64_t Sq, int64_t Lk, int32_t nh, int32_t nkv, int32_t d,
+                  int32_t causal, const int64_t *kv_len, const double *Q, const double *K,
+                  const double *V, double *ctx)
+{
+    if (Bs < 0 || Sq < 0 || Lk < 1 || nh < 1 || nkv < 1 || d < 1 || nh % nkv) return ORC_BAD_ARG;
+    if (!Q || !K || !V || !ctx) return ORC_BAD_ARG;
+    for (int64_t b = 0; b < Bs; ++b) {
+        const int64_t len = kv_len ? kv_len[b] : Lk;
+        if (len < 1 || len > Lk || (causal && len < Sq)) return ORC_BAD_ARG;
+    }
+    const int32_t G = nh / nkv;
+    const double scale = 1.0 / sqrt((double)d);
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < Bs; ++b) {
+        for (int64_t s = 0; s < Sq; ++s) {
+            const int64_t len = kv_len ? kv_len[b] : Lk;
+            const int64_t p = len - Sq + s;
+            const int64_t nkeys = causal ? p + 1 : len;
+            double *w = (double *)malloc((size_t)nkeys * sizeof(double));
+            for (int32_t h = 0; h < nh; ++h) {
+                const double *q = Q + ((b * Sq + s) * nh + h) * d;
+                const int32_t g = h / G;
+                double mx = -INFINITY;
+                for (int64_t t = 0; t < nkeys; ++t) {
+                    const double *k = K + ((b * Lk + t) * nkv + g) * d;
+                    double dot = 0.0;
+                    for (int32_t e = 0; e < d; ++e) dot += q[e] * k[e];
+                    w[t] = dot * scale;
+                    if (w[t] > mx) mx = w[t];
+                }
+                double den = 0.0;
+                for (int64_t t = 0; t < nkeys; ++t) {
+                    w[t] = exp(w[t] - mx);
+                    den += w[t];
+                }
+                double *c = ctx + ((b * Sq + s) * nh + h) * d;
+                for (int32_t e = 0; e < d; ++e) c[e] = 0.0;
+                for (int64_t t = 0; t < nkeys; ++t) {
+                    const double *v = V + ((b * Lk + t) * nkv + g) * d;
+                    for (int32_t e = 0; e < d; ++e) c[e] += w[t] * v[e];
+                }
+                for (int32_t e = 0; e < d; ++e) c[e] /= den;
+            }
+            free(w);
+        }
+    }
+    return ORC_OK;
 }
 
 void orc_set_threads(int32_t n) { if (n > 0) omp_set_num_threads(n); }

@@ -2,8 +2,9 @@
 
 Each case compiles a copy of ``oracle/oracle.c`` with one plausible mistake (a
 dropped term, a wrong constant or sign, a missing shard offset, a missing bias,
-a skipped partial, swapped gate and up operands, swapped GeLU forms) and runs
-every pin of ``test_oracle.py`` against it; at
+a skipped partial, swapped gate and up operands, swapped GeLU forms, a wrong
+attention scale, mask, head group or query position) and runs every pin of
+``test_oracle.py`` and ``test_oracle_attention.py`` against it; at
 least one pin has to fail.  Everything runs on the CPU.
 """
 import os
@@ -13,6 +14,7 @@ import pytest
 
 import oracle
 from tests import test_oracle as pins
+from tests import test_oracle_attention as attn_pins
 
 MUTANTS = {
     "gelu_no_cubic": ("0.044715 * x * x * x", "0.0 * x"),
@@ -37,21 +39,35 @@ MUTANTS = {
     "gated_up_bias_dropped": ("u[c] + bu[o + c]", "u[c]"),
     "gated_up_missing_shard_offset": ("Wu + h * F + o;", "Wu + h * F;"),
     "gated_gate_reads_up": ("const double *wg = Wg + h * F + o;", "const double *wg = Wu + h * F + o;"),
+    "linear_applies_gelu": ("if (act == ORC_ACT_NONE) return x;", "if (act == ORC_ACT_NONE) return gelu_tanh(x);"),
+    "attn_no_scale": ("w[t] = dot * scale;", "w[t] = dot;"),
+    "attn_scale_one_over_d": ("1.0 / sqrt((double)d)", "1.0 / (double)d"),
+    "attn_mask_hides_own_position": ("causal ? p + 1 : len", "causal ? (p > 0 ? p : 1) : len"),
+    "attn_mask_shows_next_position": ("causal ? p + 1 : len", "causal ? (p + 1 < len ? p + 2 : len) : len"),
+    "attn_gqa_wrong_group": ("const int32_t g = h / G;", "const int32_t g = h % nkv;"),
+    "attn_no_max_subtraction": ("w[t] = exp(w[t] - mx);", "w[t] = exp(w[t]);"),
+    "attn_not_normalised": ("c[e] /= den;", "c[e] /= 1.0;"),
+    "attn_value_of_other_key": ("V + ((b * Lk + t) * nkv + g) * d", "V + ((b * Lk + (nkeys - 1 - t)) * nkv + g) * d"),
+    "attn_queries_from_sequence_start": ("const int64_t p = len - Sq + s;", "const int64_t p = s;"),
+    "attn_key_head_offset_dropped": ("K + ((b * Lk + t) * nkv + g) * d", "K + ((b * Lk + t) * nkv) * d"),
 }
 
 
 def _all_pins():
     calls = []
-    for name in dir(pins):
-        f = getattr(pins, name)
-        if not name.startswith("test_") or not callable(f):
-            continue
-        if name == "test_shard_sum_equals_unsharded":
-            calls += [(name + "[T=%d]" % T, (lambda f=f, T=T: f(T))) for T in (1, 2, 4, 8)]
-        elif name == "test_oracle_rejects_bad_arguments":
-            continue
-        else:
-            calls.append((name, f))
+    for mod in (pins, attn_pins):
+        for name in dir(mod):
+            f = getattr(mod, name)
+            if not name.startswith("test_") or not callable(f):
+                continue
+            if name == "test_shard_sum_equals_unsharded":
+                calls += [(name + "[T=%d]" % T, (lambda f=f, T=T: f(T))) for T in (1, 2, 4, 8)]
+            elif name == "test_attn_head_shards_are_the_unsharded_heads":
+                calls += [(name + "[T=%d]" % T, (lambda f=f, T=T: f(T))) for T in (2, 4)]
+            elif name in ("test_oracle_rejects_bad_arguments", "test_attn_rejects_bad_arguments"):
+                continue
+            else:
+                calls.append((name, f))
     return calls
 
 
