@@ -17,6 +17,9 @@
  *  [GUIDE]  "Tensor parallelism" (inference guide): "Concept", "Walking
  *           through a transformer block".
  *  [GELU]   Hendrycks & Gimpel, arXiv:1606.08415 (tanh form of GeLU).
+ *  [ATTN]   Vaswani et al., arXiv:1706.03762, section 3.2 (scaled
+ *           dot-product and multi-head attention, the causal mask).
+ *  [GQA]    Ainslie et al., arXiv:2305.13245 (grouped key/value heads).
  *
  * Notation: M tokens, hidden size H, FFN width F, TP degree T, shard index
  * i in [0, T) (the pages count ranks from 1), shard width Fs = F/T, column
@@ -54,6 +57,7 @@
 #ifndef TP_COLPAR_H
 #define TP_COLPAR_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -245,6 +249,88 @@ tp_status tp_layer_fwd(float *h, void *xhat, const void *const *ctx, const void 
                        const void *W1t, const void *b1, const void *W2t, void *const *Y_ws,
                        float *const *parts, int64_t M, int64_t H, int64_t F, int32_t T,
                        hipStream_t stream);
+
+/*
+ * ---- The attention front half of rank i ----
+ * [GUIDE] "Walking through a transformer block": attention is sharded by
+ * heads (or by GQA groups of heads) across the TP ranks, and the KV cache
+ * is sharded along heads, so rank i projects and attends over its own heads
+ * only and its context ctx_i feeds the row-parallel out-projection
+ * (tp_rowpar_partial with F := A).  The attention itself is the published
+ * scaled dot-product attention ([ATTN] Vaswani et al., arXiv:1706.03762,
+ * sections 3.2.1-3.2.3, the decoder's causal mask) with grouped key/value
+ * heads ([GQA] Ainslie et al., arXiv:2305.13245).  Head dim TP_HEAD_DIM.
+ */
+#define TP_HEAD_DIM 128
+
+/*
+ * Column-parallel projection with no activation ([SLICE] column split;
+ * rank i's block C_i of the N output columns):
+ *   Y_i[m][c] = sum_h X[m][h] * W[h][i*N/T + c] + b[i*N/T + c]
+ *   Wt   W^T, [N][H] K-contiguous (full matrix); b [N] or NULL
+ *   Y_i  M rows of N/T in the input dtype, row stride ldy >= N/T elements
+ *        (lets the key and value rows of a decode step land in a cache)
+ * Validation as tp_colpar_gelu with F := N, plus ldy >= N/T and ldy % 8 == 0
+ * (TP_ERR_SHAPE / TP_ERR_UNSUPPORTED).
+ */
+tp_status tp_colpar_linear(const void *X, const void *Wt, const void *b, void *Y_i, int64_t ldy,
+                           int64_t M, int64_t H, int64_t N, int32_t T, int32_t i, tp_dtype dt,
+                           hipStream_t stream);
+
+/*
+ * Rank i's query, key and value projections in one call:
+ *   Q_i = X Wq[:, Aq_i] + bq[Aq_i]   [M][A/T],   row stride ldq
+ *   K_i = X Wk[:, Ak_i] + bk[Ak_i]   [M][Akv/T], row stride ldkv
+ *   V_i = X Wv[:, Ak_i] + bv[Ak_i]   [M][Akv/T], row stride ldkv
+ * A = nh * TP_HEAD_DIM (query width), Akv = nkv * TP_HEAD_DIM (key/value
+ * width; Akv == A without grouping); Wq_t [A][H], Wk_t and Wv_t [Akv][H]
+ * K-contiguous; biases [A] / [Akv] or NULL.  One launch when A == Akv and
+ * ldq == ldkv, else two.  Validation as tp_colpar_linear for each of the
+ * three, plus the three outputs pairwise disjoint (TP_ERR_ALIAS).
+ */
+tp_status tp_qkv_colpar(const void *X, const void *Wq_t, const void *Wk_t, const void *Wv_t,
+                        const void *bq, const void *bk, const void *bv, void *Q_i, int64_t ldq,
+                        void *K_i, void *V_i, int64_t ldkv, int64_t M, int64_t H, int64_t A,
+                        int64_t Akv, int32_t T, int32_t i, tp_dtype dt, hipStream_t stream);
+
+/*
+ * Scaled dot-product attention of one rank's heads, bf16 in and out, fp32
+ * scores, softmax and accumulation ([ATTN] 3.2.1-3.2.3, [GQA]):
+ *   ctx = softmax(q k^T / sqrt(d) over the visible keys) v   per query head
+ *   Q    [Bs*Sq][ldq]:  row b*Sq + s = query s of sequence b; query head h
+ *        at columns h*TP_HEAD_DIM (nh heads)
+ *   K, V [Bs*Lk][ldkv]: row b*Lk + t = key/value t of sequence b (its
+ *        cache of capacity Lk); head g at columns g*TP_HEAD_DIM (nkv heads)
+ *   ctx  [Bs*Sq][ldo], laid out like Q
+ *   kv_len  device int32 [Bs], the valid keys of each sequence, or NULL
+ *        (every sequence holds Lk); read on the device, values clamped to
+ *        [0, Lk]
+ * The Sq queries of sequence b are its last Sq positions: query s sits at
+ * position kv_len[b] - Sq + s.  causal != 0: it sees keys 0 .. its position;
+ * causal == 0: keys 0 .. kv_len[b]-1.  Query head h reads key/value head
+ * h / (nh / nkv).  A query row that sees no key is written as zeros.
+ * When G*Sq <= 8 (G = nh/nkv) the keys are split over many workgroups and
+ * merged in a second launch: that path needs `workspace`, a device buffer of
+ * at least tp_attn_workspace_bytes(Bs, Sq, Lk, nh, nkv) bytes (the
+ * partials; it may be reused once the call's work has run).  Otherwise the
+ * workspace is not touched and may be NULL.
+ * Validation: Bs, Sq >= 0, Lk >= 1, nh, nkv >= 1, nh % nkv == 0, causal
+ * needs Sq <= Lk, ldq and ldo >= nh*128, ldkv >= nkv*128 (TP_ERR_SHAPE);
+ * Q, K, V, ctx non-NULL, workspace non-NULL when needed (TP_ERR_NULL);
+ * d == TP_HEAD_DIM, strides multiples of 8, Q, K, V, ctx and workspace
+ * 16-byte aligned, kv_len 4-byte aligned, Sq*ldq and Lk*ldkv below 2^30
+ * (TP_ERR_UNSUPPORTED); ws_bytes too small (TP_ERR_SHAPE); ctx or workspace
+ * overlapping an input or each other (TP_ERR_ALIAS).  Bs == 0 or Sq == 0 is
+ * an empty call.
+ */
+tp_status tp_attn_core(const void *Q, const void *K, const void *V, void *ctx, const int32_t *kv_len,
+                       int64_t Bs, int64_t Sq, int64_t Lk, int32_t nh, int32_t nkv, int32_t d,
+                       int64_t ldq, int64_t ldkv, int64_t ldo, int32_t causal, void *workspace,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes tp_attn_core needs for these sizes (0: none).  Depends on
+ * the sizes only, not on the device. */
+size_t tp_attn_workspace_bytes(int64_t Bs, int64_t Sq, int64_t Lk, int32_t nh, int32_t nkv);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *tp_last_error(void);

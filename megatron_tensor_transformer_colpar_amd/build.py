@@ -24,7 +24,7 @@ CXX = os.environ.get("CXX", "g++")
 ROCM_INCLUDE = "/opt/rocm/include"
 ARCH = "gfx950"
 
-SOURCES = ["gemm_bf16.hip", "gemv_bf16.hip", "gemm_f32.hip", "reduce.hip", "abi.cpp"]
+SOURCES = ["gemm_bf16.hip", "gemv_bf16.hip", "gemm_f32.hip", "attn_bf16.hip", "reduce.hip", "abi.cpp"]
 COMMON = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 HIP_ONLY = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -61,7 +61,11 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
-    _check_no_missing_stubs(tmp)
+    try:
+        _check_no_missing_stubs(tmp)
+    except RuntimeError:
+        os.remove(tmp)
+        raise
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

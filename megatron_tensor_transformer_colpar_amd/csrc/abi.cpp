@@ -273,6 +273,74 @@ tp_status validate_group(const char *fn, const void *X, const void *W1t, const v
     return TP_OK;
 }
 
+// Column-parallel projection with no activation into Y (row stride ldy).
+tp_status validate_linear(const char *fn, const void *X, const void *Wt, const void *b, const void *Y, int64_t ldy,
+                          int64_t M, int64_t H, int64_t N, int32_t T, int32_t i, tp_dtype dt)
+{
+    tp_status st = check_shard(fn, M, H, N, T, i, dt);
+    if (st != TP_OK) return st;
+    if (ldy < N / T)
+        return fail(TP_ERR_SHAPE, "%s: row stride %lld is below N/T = %lld", fn, (long long)ldy, (long long)(N / T));
+    if (!X || !Wt || !Y) return fail(TP_ERR_NULL, "%s: X, the weight and the output must be non-NULL", fn);
+    if ((st = check_dims64(fn, H, N, T)) != TP_OK) return st;
+    if (ldy % 8 != 0 || ldy > kMaxLd)
+        return fail(TP_ERR_UNSUPPORTED, "%s: row stride %lld must be a multiple of 8 and <= 2^22", fn, (long long)ldy);
+    if (!aligned16(X) || !aligned16(Wt) || !aligned16(Y) || (b && !aligned16(b)))
+        return fail(TP_ERR_UNSUPPORTED, "%s: every buffer must be 16-byte aligned", fn);
+    if (M == 0) return TP_OK;
+    const int es = element_size(dt);
+    const Range y = span(Y, ((M - 1) * ldy + N / T) * es);
+    if (overlap(y, span(X, M * H * es)) || overlap(y, span(Wt, N * H * es)) || (b && overlap(y, span(b, N * es))))
+        return fail(TP_ERR_ALIAS, "%s: an output overlaps an input", fn);
+    return TP_OK;
+}
+
+constexpr int64_t kAttnMaxRowBytes = int64_t(1) << 31;   // per sequence, padded rows included
+
+tp_status validate_attn(const char *fn, const void *Q, const void *K, const void *V, const void *ctx,
+                        const int32_t *kv_len, int64_t Bs, int64_t Sq, int64_t Lk, int32_t nh, int32_t nkv, int32_t d,
+                        int64_t ldq, int64_t ldkv, int64_t ldo, int32_t causal, const void *ws, size_t ws_bytes)
+{
+    if (Bs < 0 || Sq < 0 || Lk < 1 || Bs > kMaxM || Sq > kMaxM || Lk > kMaxM)
+        return fail(TP_ERR_SHAPE, "%s: Bs = %lld, Sq = %lld, Lk = %lld out of range", fn, (long long)Bs,
+                    (long long)Sq, (long long)Lk);
+    if (nh < 1 || nkv < 1 || nh > 4096 || nh % nkv != 0)
+        return fail(TP_ERR_SHAPE, "%s: nh = %d, nkv = %d: need 1 <= nkv, nh <= 4096, nh %% nkv == 0", fn, nh, nkv);
+    if (causal && Sq > Lk)
+        return fail(TP_ERR_SHAPE, "%s: causal attention with more queries (%lld) than keys (%lld)", fn, (long long)Sq,
+                    (long long)Lk);
+    const int64_t A = (int64_t)nh * TP_HEAD_DIM, Akv = (int64_t)nkv * TP_HEAD_DIM;
+    if (ldq < A || ldo < A || ldkv < Akv) return fail(TP_ERR_SHAPE, "%s: a row stride is below its width", fn);
+    if (ldq > kMaxLd || ldo > kMaxLd || ldkv > kMaxLd) return fail(TP_ERR_SHAPE, "%s: a row stride exceeds 2^22", fn);
+    if (!Q || !K || !V || !ctx) return fail(TP_ERR_NULL, "%s: Q, K, V and ctx must be non-NULL", fn);
+    if (d != TP_HEAD_DIM) return fail(TP_ERR_UNSUPPORTED, "%s: head dim %d (only %d)", fn, d, TP_HEAD_DIM);
+    if (ldq % 8 || ldkv % 8 || ldo % 8) return fail(TP_ERR_UNSUPPORTED, "%s: row strides must be multiples of 8", fn);
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(ctx) || (ws && !aligned16(ws)) ||
+        (reinterpret_cast<uintptr_t>(kv_len) & 3u))
+        return fail(TP_ERR_UNSUPPORTED, "%s: misaligned buffer", fn);
+    if ((Sq + 128) * ldq * 2 >= kAttnMaxRowBytes || (Lk + 64) * ldkv * 2 >= kAttnMaxRowBytes ||
+        Bs * Sq >= kMaxM || Bs * Lk >= kMaxM || Bs * nh * ((Sq + 127) / 128) >= kMaxM)
+        return fail(TP_ERR_UNSUPPORTED, "%s: a sequence's rows exceed the kernels' 32-bit offsets", fn);
+    const tpk::AttnPlan plan = tpk::attn_plan(Bs, Sq, Lk, nh, nkv);
+    const bool need_ws = Bs > 0 && Sq > 0 && plan.decode && plan.ws_bytes > 0;
+    if (need_ws && !ws) return fail(TP_ERR_NULL, "%s: this shape needs a workspace of %zu bytes", fn, plan.ws_bytes);
+    if (need_ws && ws_bytes < plan.ws_bytes)
+        return fail(TP_ERR_SHAPE, "%s: workspace of %zu bytes, %zu needed", fn, ws_bytes, plan.ws_bytes);
+    if (Bs == 0 || Sq == 0) return TP_OK;
+    const Range o = span(ctx, ((Bs * Sq - 1) * ldo + A) * 2);
+    const Range in[4] = {span(Q, ((Bs * Sq - 1) * ldq + A) * 2), span(K, ((Bs * Lk - 1) * ldkv + Akv) * 2),
+                         span(V, ((Bs * Lk - 1) * ldkv + Akv) * 2), kv_len ? span(kv_len, Bs * 4) : Range{0, 0}};
+    for (const Range &r : in)
+        if (overlap(o, r)) return fail(TP_ERR_ALIAS, "%s: ctx overlaps an input", fn);
+    if (need_ws) {
+        const Range w = span(ws, (int64_t)plan.ws_bytes);
+        if (overlap(w, o)) return fail(TP_ERR_ALIAS, "%s: the workspace overlaps ctx", fn);
+        for (const Range &r : in)
+            if (overlap(w, r)) return fail(TP_ERR_ALIAS, "%s: the workspace overlaps an input", fn);
+    }
+    return TP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -448,6 +516,98 @@ tp_status tp_shard_reduce(const float *const *partials, int32_t T, const float *
     const hipError_t e =
         tpk::launch_shard_reduce(partials, T, residual, out_f32, out_bf16, M, H, rms, TP_RMS_EPS, stream);
     return e == hipSuccess ? ok() : hip_fail(e, "tp_shard_reduce launch");
+}
+
+tp_status tp_colpar_linear(const void *X, const void *Wt, const void *b, void *Y_i, int64_t ldy, int64_t M,
+                           int64_t H, int64_t N, int32_t T, int32_t i, tp_dtype dt, hipStream_t stream)
+{
+    const tp_status st = validate_linear("tp_colpar_linear", X, Wt, b, Y_i, ldy, M, H, N, T, i, dt);
+    if (st != TP_OK) return st;
+    if (M == 0) return ok();
+    tpk::GemmArgs g = colpar_args(X, Wt, b, &Y_i, 1, i, M, H, N, T, dt);
+    g.ldc = ldy;
+    const hipError_t e = launch(g, tpk::EPI_BIAS, dt, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "column-parallel projection launch");
+}
+
+tp_status tp_qkv_colpar(const void *X, const void *Wq_t, const void *Wk_t, const void *Wv_t, const void *bq,
+                        const void *bk, const void *bv, void *Q_i, int64_t ldq, void *K_i, void *V_i, int64_t ldkv,
+                        int64_t M, int64_t H, int64_t A, int64_t Akv, int32_t T, int32_t i, tp_dtype dt,
+                        hipStream_t stream)
+{
+    const char *fn = "tp_qkv_colpar";
+    tp_status st = validate_linear(fn, X, Wq_t, bq, Q_i, ldq, M, H, A, T, i, dt);
+    if (st != TP_OK) return st;
+    if ((st = validate_linear(fn, X, Wk_t, bk, K_i, ldkv, M, H, Akv, T, i, dt)) != TP_OK) return st;
+    if ((st = validate_linear(fn, X, Wv_t, bv, V_i, ldkv, M, H, Akv, T, i, dt)) != TP_OK) return st;
+    if (M == 0) return ok();
+    const int es = element_size(dt);
+    const Range rq = span(Q_i, ((M - 1) * ldq + A / T) * es), rk = span(K_i, ((M - 1) * ldkv + Akv / T) * es),
+                rv = span(V_i, ((M - 1) * ldkv + Akv / T) * es);
+    if (overlap(rq, rk) || overlap(rq, rv) || overlap(rk, rv))
+        return fail(TP_ERR_ALIAS, "%s: the Q, K and V outputs overlap", fn);
+    const Range wk = span(Wk_t, Akv * H * es), wv = span(Wv_t, Akv * H * es), wq = span(Wq_t, A * H * es);
+    for (const Range &o : {rq, rk, rv})
+        if (overlap(o, wq) || overlap(o, wk) || overlap(o, wv) || (bq && overlap(o, span(bq, A * es))) ||
+            (bk && overlap(o, span(bk, Akv * es))) || (bv && overlap(o, span(bv, Akv * es))))
+            return fail(TP_ERR_ALIAS, "%s: an output overlaps a weight or bias", fn);
+    if (A == Akv && ldq == ldkv) {
+        const void *W[3] = {Wq_t, Wk_t, Wv_t}, *bias[3] = {bq, bk, bv};
+        void *out[3] = {Q_i, K_i, V_i};
+        tpk::GemmArgs g = colpar_args(X, Wq_t, bq, out, 1, i, M, H, A, T, dt);
+        g.batch = 3;
+        for (int j = 0; j < 3; ++j) colpar_entry(g, j, X, W[j], bias[j], out[j], H, A / T, i, es);
+        g.ldc = ldq;
+        const hipError_t e = launch(g, tpk::EPI_BIAS, dt, stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "QKV projection launch");
+    }
+    tpk::GemmArgs gq = colpar_args(X, Wq_t, bq, &Q_i, 1, i, M, H, A, T, dt);
+    gq.ldc = ldq;
+    hipError_t e = launch(gq, tpk::EPI_BIAS, dt, stream);
+    if (e != hipSuccess) return hip_fail(e, "query projection launch");
+    void *kv[2] = {K_i, V_i};
+    tpk::GemmArgs g = colpar_args(X, Wk_t, bk, kv, 1, i, M, H, Akv, T, dt);
+    g.batch = 2;
+    colpar_entry(g, 1, X, Wv_t, bv, V_i, H, Akv / T, i, es);
+    g.ldc = ldkv;
+    e = launch(g, tpk::EPI_BIAS, dt, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "key/value projection launch");
+}
+
+tp_status tp_attn_core(const void *Q, const void *K, const void *V, void *ctx, const int32_t *kv_len, int64_t Bs,
+                       int64_t Sq, int64_t Lk, int32_t nh, int32_t nkv, int32_t d, int64_t ldq, int64_t ldkv,
+                       int64_t ldo, int32_t causal, void *workspace, size_t ws_bytes, hipStream_t stream)
+{
+    const tp_status st = validate_attn("tp_attn_core", Q, K, V, ctx, kv_len, Bs, Sq, Lk, nh, nkv, d, ldq, ldkv, ldo,
+                                       causal, workspace, ws_bytes);
+    if (st != TP_OK) return st;
+    if (Bs == 0 || Sq == 0) return ok();
+    tpk::AttnArgs a{};
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = ctx;
+    a.kv_len = kv_len;
+    a.ldq = ldq;
+    a.ldk = ldkv;
+    a.ldv = ldkv;
+    a.ldo = ldo;
+    a.Bs = Bs;
+    a.Sq = Sq;
+    a.Lk = Lk;
+    a.nh = nh;
+    a.nkv = nkv;
+    a.causal = causal != 0;
+    a.ws = workspace;
+    const hipError_t e = tpk::launch_attn_bf16(a, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "attention launch");
+}
+
+size_t tp_attn_workspace_bytes(int64_t Bs, int64_t Sq, int64_t Lk, int32_t nh, int32_t nkv)
+{
+    if (Bs < 1 || Sq < 1 || Lk < 1 || nh < 1 || nkv < 1 || nh % nkv != 0) return 0;
+    const tpk::AttnPlan p = tpk::attn_plan(Bs, Sq, Lk, nh, nkv);
+    return p.decode ? p.ws_bytes : 0;
 }
 
 const char *tp_last_error(void) { return g_err.c_str(); }

@@ -52,7 +52,9 @@ __device__ __forceinline__ float gelu_erf(float x)
 template <int EPI>
 __device__ __forceinline__ float act(float x)
 {
-    if constexpr (EPI == EPI_BIAS_GELU_ERF || EPI == EPI_GATED_ERF)
+    if constexpr (EPI == EPI_BIAS)
+        return x;
+    else if constexpr (EPI == EPI_BIAS_GELU_ERF || EPI == EPI_GATED_ERF)
         return gelu_erf(x);
     else
         return gelu_tanh(x);

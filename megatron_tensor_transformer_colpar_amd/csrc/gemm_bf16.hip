@@ -391,6 +391,7 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
     case EPI_BIAS_GELU: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU>(a, s);
     case EPI_STORE_F32: return launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32>(a, s);
     case EPI_BIAS_GELU_ERF: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU_ERF>(a, s);
+    case EPI_BIAS: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS>(a, s);
     case EPI_GATED_TANH:
         if constexpr (gated_ok) return launch_one<BM, BN, BK, S, NW, IL, EPI_GATED_TANH>(a, s);
         break;

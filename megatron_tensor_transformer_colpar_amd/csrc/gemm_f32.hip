@@ -134,6 +134,7 @@ hipError_t launch_gemm_f32(const GemmArgs &a, Epilogue epi, hipStream_t s)
             break;
         case EPI_GATED_TANH: hipLaunchKernelGGL(gemm_f32_kernel<EPI_GATED_TANH>, grid, dim3(256), 0, s, g); break;
         case EPI_GATED_ERF: hipLaunchKernelGGL(gemm_f32_kernel<EPI_GATED_ERF>, grid, dim3(256), 0, s, g); break;
+        case EPI_BIAS: hipLaunchKernelGGL(gemm_f32_kernel<EPI_BIAS>, grid, dim3(256), 0, s, g); break;
         default: return hipErrorInvalidValue;
         }
         const hipError_t e = hipGetLastError();

@@ -312,6 +312,8 @@ hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int /*num_cu*/, hip
         return two ? launch_mt<EPI_GATED_TANH, 2>(g, a.batch, s) : launch_mt<EPI_GATED_TANH, 1>(g, a.batch, s);
     case EPI_GATED_ERF:
         return two ? launch_mt<EPI_GATED_ERF, 2>(g, a.batch, s) : launch_mt<EPI_GATED_ERF, 1>(g, a.batch, s);
+    case EPI_BIAS:
+        return two ? launch_mt<EPI_BIAS, 2>(g, a.batch, s) : launch_mt<EPI_BIAS, 1>(g, a.batch, s);
     }
     return hipErrorInvalidValue;
 }

@@ -15,6 +15,7 @@ enum Epilogue : int {
     EPI_BIAS_GELU_ERF = 2,  // + bias[n] (if any), GeLU (exact x*Phi(x)), input dtype
     EPI_GATED_TANH = 3,     // GeLU_tanh(gate + bias[n]) * (up + bias2[n]), input dtype
     EPI_GATED_ERF = 4,      // GeLU_erf(gate + bias[n]) * (up + bias2[n]), input dtype
+    EPI_BIAS = 5,           // + bias[n] (if any), no activation, input dtype
 };
 constexpr bool epi_gated(int e) { return e == EPI_GATED_TANH || e == EPI_GATED_ERF; }
 
@@ -46,6 +47,30 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, Epilogue epi, int num_cu, hipStre
 hipError_t launch_gemv_bf16(const GemmArgs &g, Epilogue epi, int num_cu, hipStream_t s);
 // fp32 x fp32 -> fp32, exact fp32 FMA (no reduced-precision tricks).
 hipError_t launch_gemm_f32(const GemmArgs &g, Epilogue epi, hipStream_t s);
+
+// Scaled dot-product attention of one rank's heads, head dim 128, bf16:
+// Q rows b*Sq + s (stride ldq), K/V rows b*Lk + t (strides ldk, ldv), ctx
+// rows like Q (stride ldo); query head h at columns 128h, key/value head g
+// at columns 128g; query head h reads key/value head h / (nh / nkv).
+struct AttnArgs {
+    const void *Q, *K, *V;
+    void *O;
+    const int32_t *kv_len;   // device [Bs] valid keys per sequence, or nullptr (Lk)
+    int64_t ldq, ldk, ldv, ldo;
+    int64_t Bs, Sq, Lk;
+    int nh, nkv;
+    bool causal;
+    void *ws;                // decode partials (AttnPlan::ws_bytes), else unused
+};
+// Which kernel runs and, for the split-key decode kernel, how the keys are
+// split and how much workspace the partials take.  Depends on shapes only.
+struct AttnPlan {
+    bool decode;
+    int nsplit, chunk;
+    size_t ws_bytes;
+};
+AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv);
+hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s);
 
 // out = (residual ? residual : 0) + sum_j partials[j]; optional bf16 copy,
 // optionally row-RMS-normalised.

@@ -18,6 +18,9 @@ import numpy as np
 # tensor ids for the seed sequence
 X_ID, W1_ID, B1_ID, W2_ID, CTX_ID, WO_ID = 0, 1, 2, 3, 4, 5
 WG_ID, WU_ID, BG_ID, BU_ID = 6, 7, 8, 9   # gated first layer: gate and up weights and biases
+WQ_ID, WK_ID, WV_ID, BQ_ID, BK_ID, BV_ID = 10, 11, 12, 13, 14, 15   # attention projections
+Q_ID, K_ID, V_ID, LEN_ID = 16, 17, 18, 19                            # attention core operands
+HEAD_DIM = 128
 
 
 def f32_to_bf16_bits(x) -> np.ndarray:
@@ -184,3 +187,73 @@ def outproj_inputs(w: Workload, *, M: int | None = None, seed: int = 0, layer: i
     ctx = normal((M, As), 1.0, w.dtype, tensor=CTX_ID, **kw)
     Wo = normal((As, w.H), w.w_std, w.dtype, tensor=WO_ID, **kw)
     return ctx, Wo
+
+
+# ---------------------------------------------------------------------------
+# Attention front half: rank i's heads.  Sequences of a prefill batch are
+# consecutive token rows (row b*S + s); a decode step is one query per
+# sequence against a cache of Lk positions.
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class AttnShape:
+    wid: int
+    name: str
+    Bs: int        # sequences
+    Sq: int        # queries per sequence
+    Lk: int        # keys per sequence (cache capacity)
+    nh: int        # query heads of the rank
+    nkv: int       # key/value heads of the rank
+    H: int         # hidden size (projection input)
+    T: int         # TP degree (the full model has T * nh heads)
+    causal: bool = True
+
+
+ATTN_SHAPES = {
+    # the 8192-token prefill (4 sequences of 2048), 64 heads of 128 over 8 ranks
+    "prefill": AttnShape(6, "prefill", Bs=4, Sq=2048, Lk=2048, nh=8, nkv=8, H=8192, T=8),
+    # the 2048-token GPT-style block, 32 heads of 128 over 4 ranks
+    "gpt_block_shard": AttnShape(7, "gpt_block_shard", Bs=1, Sq=2048, Lk=2048, nh=8, nkv=8, H=4096, T=4),
+    # decode: one new token per sequence against 2048 cached positions
+    "decode": AttnShape(8, "decode", Bs=32, Sq=1, Lk=2048, nh=8, nkv=8, H=8192, T=8),
+}
+
+
+def attn_core_inputs(Bs: int, Sq: int, Lk: int, nh: int, nkv: int, *, seed: int = 0, wid: int = 0,
+                     q_std: float = 1.0, k_std: float = 1.0, v_std: float = 1.0):
+    """Q [Bs, Sq, nh*128], K and V [Bs, Lk, nkv*128], bf16, N(0, std) each."""
+    kw = dict(seed=seed, workload=wid)
+    Q = normal((Bs, Sq, nh * HEAD_DIM), q_std, "bf16", tensor=Q_ID, **kw)
+    K = normal((Bs, Lk, nkv * HEAD_DIM), k_std, "bf16", tensor=K_ID, **kw)
+    V = normal((Bs, Lk, nkv * HEAD_DIM), v_std, "bf16", tensor=V_ID, **kw)
+    return Q, K, V
+
+
+def ragged_lengths(Bs: int, lo: int, hi: int, *, seed: int = 0) -> np.ndarray:
+    """Seeded cache lengths in [lo, hi] (int32), the first and last pinned to hi and lo."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, LEN_ID, Bs, lo, hi])))
+    n = rng.integers(lo, hi + 1, size=Bs).astype(np.int32)
+    if Bs > 0:
+        n[0] = hi
+    if Bs > 1:
+        n[-1] = lo
+    return n
+
+
+def qkv_inputs(H: int, A: int, Akv: int, T: int, *, M: int, dtype: str = "bf16", seed: int = 0, wid: int = 0,
+               x_std: float = 1.0, w_std: float = 0.02, b_std: float = 0.01, shard_only: int | None = None):
+    """X [M,H], Wq [H,A], Wk [H,Akv], Wv [H,Akv], bq [A], bk [Akv], bv [Akv] (logical
+    [in, out] weights).  With ``shard_only=i`` only rank i's column blocks are
+    drawn, as stand-alone [H, A/T] / [H, Akv/T] matrices."""
+    kw = dict(seed=seed, workload=wid)
+    X = normal((M, H), x_std, dtype, tensor=X_ID, **kw)
+    if shard_only is None:
+        a, akv, sh = A, Akv, 0
+    else:
+        a, akv, sh = A // T, Akv // T, shard_only + 1
+    Wq = normal((H, a), w_std, dtype, tensor=WQ_ID, shard=sh, **kw)
+    Wk = normal((H, akv), w_std, dtype, tensor=WK_ID, shard=sh, **kw)
+    Wv = normal((H, akv), w_std, dtype, tensor=WV_ID, shard=sh, **kw)
+    bq = normal((a,), b_std, dtype, tensor=BQ_ID, shard=sh, **kw)
+    bk = normal((akv,), b_std, dtype, tensor=BK_ID, shard=sh, **kw)
+    bv = normal((akv,), b_std, dtype, tensor=BV_ID, shard=sh, **kw)
+    return X, Wq, Wk, Wv, bq, bk, bv

@@ -53,9 +53,16 @@ raw.tp_mlp_group_fwd.argtypes = [_vp, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64,
 raw.tp_layer_fwd.argtypes = [_vp, _vp, _pp, _vp, _i64, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _vp]
 raw.tp_colpar_act.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
 raw.tp_colpar_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
+raw.tp_colpar_linear.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+raw.tp_qkv_colpar.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                              _i32, _i32, _i32, _vp]
+raw.tp_attn_core.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i32,
+                             _vp, ctypes.c_size_t, _vp]
+raw.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i32]
+raw.tp_attn_workspace_bytes.restype = ctypes.c_size_t
 for _f in (raw.tp_colpar_gelu, raw.tp_rowpar_partial, raw.tp_shard_reduce, raw.tp_mlp_shard_fwd,
            raw.tp_colpar_gelu_group, raw.tp_rowpar_partial_group, raw.tp_mlp_group_fwd, raw.tp_layer_fwd,
-           raw.tp_colpar_act, raw.tp_colpar_gated):
+           raw.tp_colpar_act, raw.tp_colpar_gated, raw.tp_colpar_linear, raw.tp_qkv_colpar, raw.tp_attn_core):
     _f.restype = ctypes.c_int
 raw.tp_last_error.argtypes = []
 raw.tp_last_error.restype = ctypes.c_char_p
@@ -64,7 +71,9 @@ raw.tp_version.restype = ctypes.c_char_p
 
 EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_shard_fwd",
            "tp_colpar_gelu_group", "tp_rowpar_partial_group", "tp_mlp_group_fwd", "tp_layer_fwd",
-           "tp_colpar_act", "tp_colpar_gated", "tp_last_error", "tp_version")
+           "tp_colpar_act", "tp_colpar_gated", "tp_colpar_linear", "tp_qkv_colpar", "tp_attn_core",
+           "tp_attn_workspace_bytes", "tp_last_error", "tp_version")
+TP_HEAD_DIM = 128
 
 
 class TPError(RuntimeError):
@@ -157,3 +166,23 @@ def tp_colpar_gated(X, Wgt, Wut, bg, bu, Y_i, M, H, F, T, i, act, dt=TP_BF16, st
 def tp_layer_fwd(h, xhat, ctx, Wot, A, W1t, b1, W2t, Y_ws, parts, M, H, F, T, stream=None):
     _check(raw.tp_layer_fwd(_ptr(h), _ptr(xhat), _arr(ctx), _ptr(Wot), A, _ptr(W1t), _ptr(b1), _ptr(W2t),
                             _arr(Y_ws), _arr(parts), M, H, F, T, _stream(stream)))
+
+
+def tp_colpar_linear(X, Wt, b, Y_i, ldy, M, H, N, T, i, dt=TP_BF16, stream=None):
+    _check(raw.tp_colpar_linear(_ptr(X), _ptr(Wt), _ptr(b), _ptr(Y_i), ldy, M, H, N, T, i, dt, _stream(stream)))
+
+
+def tp_qkv_colpar(X, Wq_t, Wk_t, Wv_t, bq, bk, bv, Q_i, ldq, K_i, V_i, ldkv, M, H, A, Akv, T, i, dt=TP_BF16,
+                  stream=None):
+    _check(raw.tp_qkv_colpar(_ptr(X), _ptr(Wq_t), _ptr(Wk_t), _ptr(Wv_t), _ptr(bq), _ptr(bk), _ptr(bv), _ptr(Q_i),
+                             ldq, _ptr(K_i), _ptr(V_i), ldkv, M, H, A, Akv, T, i, dt, _stream(stream)))
+
+
+def tp_attn_core(Q, K, V, ctx, kv_len, Bs, Sq, Lk, nh, nkv, d, ldq, ldkv, ldo, causal, workspace, ws_bytes,
+                 stream=None):
+    _check(raw.tp_attn_core(_ptr(Q), _ptr(K), _ptr(V), _ptr(ctx), _ptr(kv_len), Bs, Sq, Lk, nh, nkv, d, ldq, ldkv,
+                            ldo, int(bool(causal)), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tp_attn_workspace_bytes(Bs, Sq, Lk, nh, nkv) -> int:
+    return int(raw.tp_attn_workspace_bytes(Bs, Sq, Lk, nh, nkv))

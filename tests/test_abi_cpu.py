@@ -21,7 +21,7 @@ P = [0x10000000 * (k + 1) for k in range(12)]
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:tp_status|const char \*)\s*(tp_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:tp_status|const char \*|size_t)\s*(tp_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_boundary():
@@ -274,4 +274,95 @@ def test_variant_empty_calls_are_ok():
     assert colpar_act(M=0) == tp.TP_OK
     assert gated(M=0) == tp.TP_OK
     assert gated(M=0, bg=None, bu=None, act=tp.TP_GELU_ERF) == tp.TP_OK
+    assert tp.last_error() == ""
+
+
+# ------------------------------------------------ attention front half
+def linear(X=P[0], W=P[1], b=P[2], Y=P[3], ldy=64, M=4, H=64, N=256, T=4, i=0, dt=BF16):
+    return tp.raw.tp_colpar_linear(X, W, b, Y, ldy, M, H, N, T, i, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), tp.TP_ERR_SHAPE),
+    (dict(T=3), tp.TP_ERR_SHAPE),
+    (dict(ldy=56), tp.TP_ERR_SHAPE),          # below N/T
+    (dict(W=None), tp.TP_ERR_NULL),
+    (dict(Y=None), tp.TP_ERR_NULL),
+    (dict(ldy=68), tp.TP_ERR_UNSUPPORTED),    # not a multiple of 8
+    (dict(H=96), tp.TP_ERR_UNSUPPORTED),
+    (dict(b=P[2] + 4), tp.TP_ERR_UNSUPPORTED),
+    (dict(Y=P[1] + 64), tp.TP_ERR_ALIAS),     # Y over the weight
+    (dict(Y=P[0] + 2, X=P[0]), tp.TP_ERR_UNSUPPORTED),
+])
+def test_colpar_linear_rejects(kw, status):
+    assert linear(**kw) == status
+    assert "tp_colpar_linear" in tp.last_error()
+
+
+def qkv(X=P[0], Wq=P[1], Wk=P[2], Wv=P[3], bq=P[4], bk=P[5], bv=P[6], Q=P[7], ldq=64, K=P[8], V=P[9], ldkv=64,
+        M=4, H=64, A=256, Akv=256, T=4, i=0, dt=BF16):
+    return tp.raw.tp_qkv_colpar(X, Wq, Wk, Wv, bq, bk, bv, Q, ldq, K, V, ldkv, M, H, A, Akv, T, i, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(i=4), tp.TP_ERR_SHAPE),
+    (dict(Akv=202), tp.TP_ERR_SHAPE),         # not divisible by T
+    (dict(Akv=200), tp.TP_ERR_UNSUPPORTED),   # Akv/T not a multiple of 64
+    (dict(Wk=None), tp.TP_ERR_NULL),
+    (dict(V=None), tp.TP_ERR_NULL),
+    (dict(ldkv=60), tp.TP_ERR_SHAPE),
+    (dict(K=P[7] + 128), tp.TP_ERR_ALIAS),    # K over Q
+    (dict(V=P[8]), tp.TP_ERR_ALIAS),          # V over K
+    (dict(Q=P[3] + 256), tp.TP_ERR_ALIAS),    # Q over Wv
+])
+def test_qkv_rejects(kw, status):
+    assert qkv(**kw) == status
+    assert "tp_qkv_colpar" in tp.last_error()
+
+
+def attn(Q=P[0], K=P[1], V=P[2], ctx=P[3], kv_len=None, Bs=2, Sq=256, Lk=256, nh=8, nkv=8, d=128, ldq=1024,
+         ldkv=1024, ldo=1024, causal=1, ws=None, ws_bytes=0):
+    return tp.raw.tp_attn_core(Q, K, V, ctx, kv_len, Bs, Sq, Lk, nh, nkv, d, ldq, ldkv, ldo, causal, ws, ws_bytes,
+                               None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Bs=-1), tp.TP_ERR_SHAPE),
+    (dict(Lk=0), tp.TP_ERR_SHAPE),
+    (dict(nkv=3), tp.TP_ERR_SHAPE),           # nh % nkv
+    (dict(Sq=300), tp.TP_ERR_SHAPE),          # causal, more queries than keys
+    (dict(ldq=1000), tp.TP_ERR_SHAPE),        # below nh * 128
+    (dict(ldkv=512), tp.TP_ERR_SHAPE),
+    (dict(Q=None), tp.TP_ERR_NULL),
+    (dict(ctx=None), tp.TP_ERR_NULL),
+    (dict(d=64), tp.TP_ERR_UNSUPPORTED),
+    (dict(ldo=1028), tp.TP_ERR_UNSUPPORTED),  # not a multiple of 8
+    (dict(K=P[1] + 8), tp.TP_ERR_UNSUPPORTED),
+    (dict(kv_len=P[4] + 2), tp.TP_ERR_UNSUPPORTED),
+    (dict(Sq=1, Lk=1 << 20), tp.TP_ERR_UNSUPPORTED),   # rows beyond 32-bit offsets
+    (dict(Sq=1), tp.TP_ERR_NULL),             # the split-key path needs a workspace
+    (dict(Sq=1, ws=P[5], ws_bytes=16), tp.TP_ERR_SHAPE),
+    (dict(ctx=P[0] + 2048), tp.TP_ERR_ALIAS),
+    (dict(Sq=1, ws=P[1] + 4096, ws_bytes=1 << 20), tp.TP_ERR_ALIAS),
+])
+def test_attn_core_rejects(kw, status):
+    assert attn(**kw) == status
+    assert "tp_attn_core" in tp.last_error()
+
+
+def test_attn_workspace_bytes():
+    # prefill shapes need none; the split-key decode path needs its partials
+    assert tp.tp_attn_workspace_bytes(4, 2048, 2048, 8, 8) == 0
+    n = tp.tp_attn_workspace_bytes(8, 1, 2048, 8, 8)
+    assert n > 0 and n % (8 * 8 * 130 * 4) == 0
+    assert tp.tp_attn_workspace_bytes(0, 1, 2048, 8, 8) == 0
+    assert tp.tp_attn_workspace_bytes(1, 1, 2048, 8, 3) == 0     # invalid grouping
+    assert attn(Bs=8, Sq=1, Lk=2048, ws=P[5], ws_bytes=n - 4) == tp.TP_ERR_SHAPE
+
+
+def test_attention_empty_calls_are_ok():
+    assert linear(M=0) == tp.TP_OK
+    assert qkv(M=0) == tp.TP_OK
+    assert attn(Bs=0) == tp.TP_OK
+    assert attn(Sq=0, causal=0) == tp.TP_OK
     assert tp.last_error() == ""
