@@ -22,6 +22,10 @@ Also reported on the same JSON line:
                 layer) at decode M=8 (weight GB/s) and prefill M=4096 (TFLOP/s)
   variants      rank 0's exact-GeLU and gated Gate/Up first layer: prefill
                 (TFLOP/s) and gated decode at M=8 (weight GB/s)
+  attention     rank 0's attention front half (8 heads of 128, H=8192):
+                prefill of 4 x 2048 tokens (Q/K/V projection, causal
+                attention, out-projection; TFLOP/s) and decode of M in
+                {1, 8, 32} sequences over 2048 cached positions (GB/s)
   hipblaslt_context  the column-parallel launches next to torch.matmul
                 (hipBLASLt) on the same shapes, same GPU, same run
   cpu_baseline  the fp64 oracle on a bounded sample of the headline rows
@@ -264,6 +268,107 @@ def variants(args, torch, tp):
     return out
 
 
+def attention(args, torch, tp):
+    """The attention front half of rank 0 (8 heads of 128 at H=8192, T=8).
+    Prefill, 4 sequences of 2048 tokens: the Q/K/V projection (one launch of
+    three problems), causal attention on the matrix cores, the row-parallel
+    out-projection (TFLOP/s; attention counts 4*d flops per visible
+    query-key pair).  Decode, M sequences of 2048 cached positions, one new
+    token each: the Q/K/V projection writing the new key and value rows into
+    the caches, and split-key attention over the caches (HBM GB/s of weights
+    or cache bytes; weight sets and caches rotate over more than 1 GiB, so
+    every call streams from HBM)."""
+    g = torch.Generator(device="cuda").manual_seed(11)
+    stream = torch.cuda.current_stream().cuda_stream
+    H, As, D, nh = 8192, 1024, 128, 8
+
+    def bf(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+    def timed(f, n):
+        for k in range(3):
+            f(k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(n):
+            f(k)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def rate(flops, ms):
+        t = flops / (ms * 1e-3) / 1e12
+        return {"us": round(ms * 1e3, 2), "tflops": round(t, 1), "frac": round(t / PEAK_BF16_TFLOPS, 4)}
+
+    def bw(nbytes, ms):
+        b = nbytes / (ms * 1e-3) / 1e9
+        return {"us": round(ms * 1e3, 2), "gbs": round(b, 1), "frac": round(b / PEAK_HBM_GBS, 4)}
+
+    out = {}
+    n = max(5, args.steps // 5)
+    # ---- prefill
+    Bs, S = 4, 2048
+    M = Bs * S
+    X = bf(M, H)
+    Wq, Wk, Wv = (bf(As, H, std=0.02) for _ in range(3))
+    Wo = bf(H, As, std=0.02)
+    bq, bk, bv = bf(As, std=0.01), bf(As, std=0.01), bf(As, std=0.01)
+    Q, K, V = (torch.empty(M, As, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    ctx = torch.empty(M, As, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    qkv = lambda k: tp.tp_qkv_colpar(X, Wq, Wk, Wv, bq, bk, bv, Q, As, K, V, As, M, H, As, As, 1, 0, tp.TP_BF16,
+                                     stream)
+    core = lambda k: tp.tp_attn_core(Q, K, V, ctx, None, Bs, S, S, nh, nh, D, As, As, As, 1, None, 0, stream)
+    oproj = lambda k: tp.tp_rowpar_partial(ctx, Wo, Z, M, H, As, 1, 0, tp.TP_BF16, stream)
+    pairs = Bs * nh * S * (S + 1) / 2
+    pre = {"workload": "rank 0, 4 sequences x 2048 tokens, H=8192, 8 heads x 128, causal",
+           "qkv_projection": rate(2.0 * M * H * 3 * As, timed(qkv, n)),
+           "attention_core": rate(4.0 * D * pairs, timed(core, n)),
+           "out_projection": rate(2.0 * M * As * H, timed(oproj, n))}
+    out["prefill"] = pre
+    log("[bench] attention prefill: %s" % pre)
+    del X, Q, K, V, ctx, Z, Wq, Wk, Wv, Wo
+    torch.cuda.empty_cache()
+    # ---- decode
+    L = 2048
+    R = args.decode_sets
+    wsets = [(bf(As, H, std=0.02), bf(As, H, std=0.02), bf(As, H, std=0.02)) for _ in range(R)]
+    dec = {}
+    for Bs in (1, 8, 32):
+        cache_bytes = Bs * L * As * 2 * 2
+        C = max(2, -(-(1 << 30) // cache_bytes))
+        caches = [(bf(Bs * L, As), bf(Bs * L, As)) for _ in range(C)]
+        X = bf(Bs, H)
+        Q = torch.empty(Bs, As, dtype=torch.bfloat16, device="cuda")
+        ctx = torch.empty(Bs, As, dtype=torch.bfloat16, device="cuda")
+        nws = tp.tp_attn_workspace_bytes(Bs, 1, L, nh, nh)
+        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+
+        def qkv(k):
+            wq, wk, wv = wsets[k % R]
+            kc, vc = caches[k % C]
+            tp.tp_qkv_colpar(X, wq, wk, wv, bq, bk, bv, Q, As, kc[L - 1:], vc[L - 1:], L * As, Bs, H, As, As, 1, 0,
+                             tp.TP_BF16, stream)
+
+        def core(k):
+            kc, vc = caches[k % C]
+            tp.tp_attn_core(Q, kc, vc, ctx, None, Bs, 1, L, nh, nh, D, As, As, As, 1, ws, nws, stream)
+
+        nd = max(2 * max(R, C), args.steps)
+        wbytes = 3.0 * (As * H * 2 + As * 2) + Bs * H * 2 + 3 * Bs * As * 2
+        e = {"qkv_projection": bw(wbytes, timed(qkv, nd)),
+             "attention_core": bw(cache_bytes + 2.0 * Bs * As * 2, timed(core, nd)),
+             "cache_bytes": cache_bytes}
+        dec["M=%d" % Bs] = e
+        log("[bench] attention decode M=%d: %s" % (Bs, e))
+        del caches, X, Q, ctx, ws
+        torch.cuda.empty_cache()
+    dec["workload"] = "rank 0, M sequences each with 2048 cached positions, 8 heads x 128, H=8192"
+    out["decode"] = dec
+    return out
+
+
 def hipblaslt_context(args, torch, tp):
     """The library's column-parallel launches next to hipBLASLt (torch.matmul,
     bf16 out, no bias or GeLU) on the same shapes, timed alternately on the
@@ -474,7 +579,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline step only (for profiling)")
-    ap.add_argument("--sections", default="prefill,decode,stack80,variants,context",
+    ap.add_argument("--sections", default="prefill,decode,stack80,variants,attention,context",
                     help="comma-separated extra sections to run after the headline step")
     ap.add_argument("--context-only", action="store_true",
                     help="only the library-vs-hipBLASLt comparison (for counter runs)")
@@ -531,6 +636,9 @@ def main():
         rec["stack80"] = stack80(args, torch, tp)
     if "variants" in sections:
         rec["variants"] = variants(args, torch, tp)
+    if "attention" in sections:
+        rec["attention"] = attention(args, torch, tp)
+        torch.cuda.empty_cache()
     if "context" in sections:
         rec["hipblaslt_context"] = hipblaslt_context(args, torch, tp)
     if not args.no_cpu_baseline:

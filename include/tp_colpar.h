@@ -284,8 +284,8 @@ tp_status tp_colpar_linear(const void *X, const void *Wt, const void *b, void *Y
  *   V_i = X Wv[:, Ak_i] + bv[Ak_i]   [M][Akv/T], row stride ldkv
  * A = nh * TP_HEAD_DIM (query width), Akv = nkv * TP_HEAD_DIM (key/value
  * width; Akv == A without grouping); Wq_t [A][H], Wk_t and Wv_t [Akv][H]
- * K-contiguous; biases [A] / [Akv] or NULL.  One launch when A == Akv and
- * ldq == ldkv, else two.  Validation as tp_colpar_linear for each of the
+ * K-contiguous; biases [A] / [Akv] or NULL.  One launch when A == Akv,
+ * else two.  Validation as tp_colpar_linear for each of the
  * three, plus the three outputs pairwise disjoint (TP_ERR_ALIAS).
  */
 tp_status tp_qkv_colpar(const void *X, const void *Wq_t, const void *Wk_t, const void *Wv_t,

@@ -551,13 +551,14 @@ tp_status tp_qkv_colpar(const void *X, const void *Wq_t, const void *Wk_t, const
         if (overlap(o, wq) || overlap(o, wk) || overlap(o, wv) || (bq && overlap(o, span(bq, A * es))) ||
             (bk && overlap(o, span(bk, Akv * es))) || (bv && overlap(o, span(bv, Akv * es))))
             return fail(TP_ERR_ALIAS, "%s: an output overlaps a weight or bias", fn);
-    if (A == Akv && ldq == ldkv) {
+    if (A == Akv) {
         const void *W[3] = {Wq_t, Wk_t, Wv_t}, *bias[3] = {bq, bk, bv};
         void *out[3] = {Q_i, K_i, V_i};
         tpk::GemmArgs g = colpar_args(X, Wq_t, bq, out, 1, i, M, H, A, T, dt);
         g.batch = 3;
         for (int j = 0; j < 3; ++j) colpar_entry(g, j, X, W[j], bias[j], out[j], H, A / T, i, es);
         g.ldc = ldq;
+        g.ldc_b[1] = g.ldc_b[2] = ldkv;
         const hipError_t e = launch(g, tpk::EPI_BIAS, dt, stream);
         return e == hipSuccess ? ok() : hip_fail(e, "QKV projection launch");
     }
@@ -599,7 +600,7 @@ tp_status tp_attn_core(const void *Q, const void *K, const void *V, void *ctx, c
     a.nkv = nkv;
     a.causal = causal != 0;
     a.ws = workspace;
-    const hipError_t e = tpk::launch_attn_bf16(a, stream);
+    const hipError_t e = tpk::launch_attn_bf16(a, num_cu(), stream);
     return e == hipSuccess ? ok() : hip_fail(e, "attention launch");
 }
 

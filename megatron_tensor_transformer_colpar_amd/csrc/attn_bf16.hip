@@ -49,6 +49,7 @@ constexpr int kBK = 64;           // keys per tile
 constexpr int kSlots = kBK * kD / 8;  // 16-byte slots per K or V tile (16 KiB)
 constexpr int kDecRows = 8;       // most query rows per key/value head on the decode kernel
 constexpr int kDecMaxChunk = 512; // most keys per decode workgroup
+constexpr int kMaxSplit = 4096;   // most key chunks per sequence on the decode path
 
 struct AttnDev {
     const __bf16 *Q, *K, *V;
@@ -78,16 +79,34 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //     consecutive rows, one chunk) hits 16 different slots.
 //  V: chunk c of row r sits at slot c ^ 4(r & 3): a transpose read (4
 //     consecutive rows x 4 chunks per 32 lanes) hits 16 different slots.
-__global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt)
+// Causal query tiles differ in cost (tile qt walks about qt+1 key tiles).
+// Items are ranked by cost, heaviest first.  When every workgroup is
+// resident at once (grid <= resident), workgroup i of the first half takes
+// item i and workgroup i of the second half the item of mirrored rank, so
+// the two workgroups that share a CU sum to about the same cost; otherwise
+// workgroups take items heaviest first as slots free up.
+__device__ __forceinline__ int item_of_block(int bid, int grid, int resident)
 {
-    __shared__ u32x4 k_lds[2][kSlots];
-    __shared__ u32x4 v_lds[2][kSlots];
+    if (grid > resident) return bid;
+    const int half = (grid + 1) / 2;
+    return bid < half ? bid : grid - 1 - (bid - half);
+}
+
+__global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt, int resident)
+{
+    // one array per stage and operand: the compiler then knows which tile
+    // a read touches and does not wait for the DMA filling the other stage
+    __shared__ u32x4 k0_lds[kSlots];
+    __shared__ u32x4 v0_lds[kSlots];
+    __shared__ u32x4 k1_lds[kSlots];
+    __shared__ u32x4 v1_lds[kSlots];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int per_qt = a.Bs * a.nh;
-    const int qt = nqt - 1 - (int)blockIdx.x / per_qt;  // longest causal rows first
-    const int rem = (int)blockIdx.x % per_qt;
+    const int item = item_of_block((int)blockIdx.x, (int)gridDim.x, resident);
+    const int qt = nqt - 1 - item / per_qt;   // items ranked by cost
+    const int rem = item % per_qt;
     const int b = rem / a.nh, hq = rem % a.nh, g = hq / a.G;
     const int len = seq_len(a, b);
     const int off = len - a.Sq;                          // position of query s is off + s
@@ -128,16 +147,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt)
     const uint32_t k_jstep = (uint32_t)(16 * a.ldk * 2), v_jstep = (uint32_t)(16 * a.ldv * 2);
     const uint32_t k_tstep = (uint32_t)(kBK * a.ldk * 2), v_tstep = (uint32_t)(kBK * a.ldv * 2);
 
-    auto issue = [&](int stage, int kt) __attribute__((always_inline)) {
+    auto issue = [&](u32x4 *kst, u32x4 *vst, int kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t vo = k_vo + j * k_jstep + kt * k_tstep;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(&k_lds[stage][(4 * j + wave) * 64]), 16, vo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, LDS_PTR(kst + (4 * j + wave) * 64), 16, vo, 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t vo = v_vo + j * v_jstep + kt * v_tstep;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(&v_lds[stage][(4 * j + wave) * 64]), 16, vo, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, LDS_PTR(vst + (4 * j + wave) * 64), 16, vo, 0, 0, 0);
         }
     };
 
@@ -150,8 +169,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt)
     const int vlow = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     const int vbyte = (4 * h + rr) * 256 + 16 * vlow + 8 * (lane & 1);
 
-    if (ntiles > 0) issue(0, 0);
-    if (ntiles > 1) issue(1, 1);
+    if (ntiles > 0) issue(k0_lds, v0_lds, 0);
+    if (ntiles > 1) issue(k1_lds, v1_lds, 1);
 
     float m_run = -1e30f, l_run = 0.0f;
     f32x16 acc[4];
@@ -159,8 +178,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt)
     for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
     const int my_pos = off + q0 + col;
 
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int st = kt & 1;
+    // one key tile from the stage (kst, vst), which is then refilled with tile kt + 2
+    auto tile = [&](int kt, u32x4 *kst, u32x4 *vst) __attribute__((always_inline)) {
         if (kt + 1 < ntiles)
             __builtin_amdgcn_s_waitcnt(wait_vm(8));
         else
@@ -176,44 +195,54 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int row = kb * 32 + col;
-                    const bf16x8 kf = __builtin_bit_cast(bf16x8, k_lds[st][kfrag + kb * 512 + ((2 * t + h) ^ (row & 15))]);
+                    const bf16x8 kf = __builtin_bit_cast(bf16x8, kst[kfrag + kb * 512 + ((2 * t + h) ^ (row & 15))]);
                     s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
                 }
             }
-            // lane: query q0 + col; element r of s[kb]: key k0 + 32kb + 8(r/4) + 4h + r%4
-            const bool need_mask = (k0 + kBK > len) || (a.causal && k0 + kBK - 1 > off + q0);
+            // lane: query q0 + col; element r of s[kb]: key k0 + 32kb + 8(r/4) + 4h + r%4.
+            // Only tiles on the diagonal or past the sequence's end need the mask.
+            if ((k0 + kBK > len) || (a.causal && k0 + kBK - 1 > off + q0)) {
+                const int lim = a.causal ? min(len - 1, my_pos) : len - 1;   // last visible key
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        s[kb][r] = key > lim ? -INFINITY : s[kb][r];
+                    }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = s[kb][r] * a.scale_log2;
-                    if (need_mask) {
-                        const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (key >= len || (a.causal && key > my_pos)) x = -INFINITY;
-                    }
-                    s[kb][r] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - m_new);
-            m_run = m_new;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+            // Lazy rescale: the reference max m_run (log2 units) only moves
+            // when a tile's max exceeds it by more than 8, so the weights stay
+            // <= 2^8 and the output is rescaled only on those tiles; the sum
+            // and the output share the reference, so the result is the same.
+            const bool grow = mx > m_run + 8.0f;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                const float m_new = grow ? mx : m_run;
+                const float alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+            }
             float ls = 0.0f;
             bf16x8 pb[2][2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(s[kb][r] - m_new);
+                    const float p = fast_exp2(fmaf(s[kb][r], a.scale_log2, -m_run));
                     ls += p;
                     pb[kb][r >> 3][r & 7] = (__bf16)p;
                 }
-            l_run = l_run * alpha + ls;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+            l_run += ls;
             // O^T += V^T P^T; k-slot e of lane half h is key 16ks + 8(e/4) + 4h + e%4 of block kb
-            const lds_char *vt = reinterpret_cast<const lds_char *>(LDS_PTR(&v_lds[st][0]));
+            const lds_char *vt = reinterpret_cast<const lds_char *>(LDS_PTR(vst));
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -232,7 +261,11 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt)
         // every wave is done with this stage before it is refilled
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();
-        if (kt + 2 < ntiles) issue(st, kt + 2);
+        if (kt + 2 < ntiles) issue(kst, vst, kt + 2);
+    };
+    for (int kt = 0; kt < ntiles; kt += 2) {
+        tile(kt, k0_lds, v0_lds);
+        if (kt + 1 < ntiles) tile(kt + 1, k1_lds, v1_lds);
     }
 
     // normalise and store: lane holds query q0 + col, dims 32db + 8(r/4) + 4h + r%4
@@ -417,32 +450,54 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, 
     }
 }
 
-// One workgroup per (b, s, head) query row, one lane per dim.
+// One workgroup per (b, s, head) query row, one lane per dim.  The chunks'
+// maxima and sums are read in parallel (lane c takes chunk c, c + 128, ...)
+// and reduced through LDS; the weighted rows are then summed with eight
+// loads in flight per lane.
 __global__ void __launch_bounds__(kD) attn_combine_kernel(AttnDev a, int nsplit, const float *ws_o,
                                                           const float *ws_ml)
 {
-    const int d = threadIdx.x;
+    __shared__ float red[kD / 64];
+    __shared__ float wts[kMaxSplit];
+    const int t = threadIdx.x;
     const int64_t qrow = blockIdx.x;   // (b * Sq + s) * nh + hq
     const int64_t stride = (int64_t)a.Bs * a.Sq * a.nh;
     float M = -INFINITY;
-    for (int c = 0; c < nsplit; ++c) {
-        const int64_t row = c * stride + qrow;
-        if (ws_ml[2 * row + 1] > 0.0f) M = fmaxf(M, ws_ml[2 * row]);
+    for (int c = t; c < nsplit; c += kD) {
+        const float2 ml = *reinterpret_cast<const float2 *>(ws_ml + 2 * (c * stride + qrow));
+        if (ml.y > 0.0f) M = fmaxf(M, ml.x);
     }
-    float L = 0.0f, O = 0.0f;
-    if (M > -INFINITY)
-        for (int c = 0; c < nsplit; ++c) {
-            const int64_t row = c * stride + qrow;
-            const float l = ws_ml[2 * row + 1];
-            if (l > 0.0f) {
-                const float w = fast_exp2(ws_ml[2 * row] - M);
-                L = fmaf(l, w, L);
-                O = fmaf(ws_o[row * kD + d], w, O);
-            }
-        }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+    if ((t & 63) == 0) red[t >> 6] = M;
+    __syncthreads();
+    M = fmaxf(red[0], red[1]);
+    __syncthreads();
+    float L = 0.0f;
+    for (int c = t; c < nsplit; c += kD) {
+        const float2 ml = *reinterpret_cast<const float2 *>(ws_ml + 2 * (c * stride + qrow));
+        const float w = ml.y > 0.0f ? fast_exp2(ml.x - M) : 0.0f;
+        wts[c] = w;
+        L = fmaf(ml.y, w, L);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m);
+    if ((t & 63) == 0) red[t >> 6] = L;
+    __syncthreads();
+    L = red[0] + red[1];
+    float O = 0.0f;
+    int c = 0;
+    for (; c + 8 <= nsplit; c += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = ws_o[((c + u) * stride + qrow) * kD + t];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) O = fmaf(v[u], wts[c + u], O);
+    }
+    for (; c < nsplit; ++c) O = fmaf(ws_o[(c * stride + qrow) * kD + t], wts[c], O);
     const int64_t bs = qrow / a.nh;
     const int hq = (int)(qrow % a.nh);
-    a.O[bs * a.ldo + hq * kD + d] = (__bf16)(L > 0.0f ? O / L : 0.0f);
+    a.O[bs * a.ldo + hq * kD + t] = (__bf16)(L > 0.0f ? O / L : 0.0f);
 }
 
 template <int NR>
@@ -472,6 +527,10 @@ AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv)
     int64_t chunk = (Lk + nsplit - 1) / nsplit;
     chunk = (chunk + 63) / 64 * 64;
     nsplit = (Lk + chunk - 1) / chunk;
+    if (nsplit > kMaxSplit) {   // caches beyond 2M keys take the matrix-core kernel
+        p.decode = false;
+        return p;
+    }
     p.nsplit = (int)nsplit;
     p.chunk = (int)chunk;
     const int64_t qrows = Bs * Sq * nh;
@@ -479,7 +538,7 @@ AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv)
     return p;
 }
 
-hipError_t launch_attn_bf16(const AttnArgs &x, hipStream_t s)
+hipError_t launch_attn_bf16(const AttnArgs &x, int num_cu, hipStream_t s)
 {
     AttnDev d{};
     d.Q = static_cast<const __bf16 *>(x.Q);
@@ -503,7 +562,8 @@ hipError_t launch_attn_bf16(const AttnArgs &x, hipStream_t s)
     if (!p.decode) {
         const int nqt = (int)((x.Sq + kBQ - 1) / kBQ);
         const int64_t grid = (int64_t)nqt * x.Bs * x.nh;
-        hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(256), 0, s, d, nqt);
+        // two workgroups per CU (64 KiB of LDS and <= 256 VGPRs each)
+        hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(256), 0, s, d, nqt, 2 * num_cu);
         return hipGetLastError();
     }
     float *ws_o = static_cast<float *>(x.ws);

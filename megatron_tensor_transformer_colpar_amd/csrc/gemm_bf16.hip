@@ -38,7 +38,8 @@ struct GemmDev {
     const __bf16 *B2[kMaxBatch];     // gated epilogues: up rows
     const __bf16 *bias2[kMaxBatch];  // gated epilogues: up bias
     void *C[kMaxBatch];
-    int64_t lda, ldb, ldc;
+    int64_t lda, ldb;
+    int64_t ldc[kMaxBatch];
     int M, N, K;
     int tiles_m, tiles_n, batch;
 };
@@ -111,6 +112,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     const __bf16 *const Bbase = g.B[bt];
     const __bf16 *const bias_p = g.bias[bt];
     void *const Cbase = g.C[bt];
+    const int64_t ldc = g.ldc[bt];
 
     const int a_rows = min(BM, g.M - m0), b_rows = min(BNO, g.N - n0);
     const __amdgpu_buffer_rsrc_t ra =
@@ -321,7 +323,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
                                            acc[i][ju][4 * q + 3]} + bu[q];
                     const bf16x4 y = {(__bf16)(act<EPI>(ga[0]) * up[0]), (__bf16)(act<EPI>(ga[1]) * up[1]),
                                       (__bf16)(act<EPI>(ga[2]) * up[2]), (__bf16)(act<EPI>(ga[3]) * up[3])};
-                    *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * g.ldc + n) = y;
+                    *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * ldc + n) = y;
                 }
             }
         }
@@ -342,12 +344,12 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
                     if (!full && n >= g.N) continue;
                     f32x4 x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                     if (EPI == EPI_STORE_F32) {
-                        *reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * g.ldc + n) = x;
+                        *reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n) = x;
                     } else {
                         x += bias[q];
                         const bf16x4 y = {(__bf16)act<EPI>(x[0]), (__bf16)act<EPI>(x[1]), (__bf16)act<EPI>(x[2]),
                                           (__bf16)act<EPI>(x[3])};
-                        *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * g.ldc + n) = y;
+                        *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * ldc + n) = y;
                     }
                 }
             }
@@ -370,7 +372,7 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
     }
     g.lda = a.lda;
     g.ldb = a.ldb;
-    g.ldc = a.ldc;
+    for (int b = 0; b < kMaxBatch; ++b) g.ldc[b] = ldc_of(a, b < a.batch ? b : 0);
     g.M = (int)a.M;
     g.N = (int)a.N;
     g.K = (int)a.K;

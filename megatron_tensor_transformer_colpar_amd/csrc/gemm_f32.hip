@@ -120,7 +120,7 @@ hipError_t launch_gemm_f32(const GemmArgs &a, Epilogue epi, hipStream_t s)
         g.C = static_cast<float *>(a.C[b]);
         g.lda = a.lda;
         g.ldb = a.ldb;
-        g.ldc = a.ldc;
+        g.ldc = ldc_of(a, b);
         g.M = (int)a.M;
         g.N = (int)a.N;
         g.K = (int)a.K;

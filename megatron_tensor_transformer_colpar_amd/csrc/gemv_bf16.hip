@@ -30,7 +30,8 @@ struct GemvDev {
     const __bf16 *W2[kMaxBatch];     // gated epilogues: up rows
     const __bf16 *bias2[kMaxBatch];  // gated epilogues: up bias
     void *C[kMaxBatch];
-    int64_t ldx, ldw, ldc;
+    int64_t ldx, ldw;
+    int64_t ldc[kMaxBatch];
     int M, N, K;
 };
 
@@ -62,15 +63,15 @@ __device__ __forceinline__ void gemv_store(const GemvDev &g, int bt, int n0, int
         const float bg = g.bias[bt] ? (float)g.bias[bt][n] : 0.0f;
         const float bu = g.bias2[bt] ? (float)g.bias2[bt][n] : 0.0f;
         const float y = act<EPI>(sum(idx) + bg) * (sum(idx + 32) + bu);
-        static_cast<__bf16 *>(g.C[bt])[(int64_t)m * g.ldc + n] = (__bf16)y;
+        static_cast<__bf16 *>(g.C[bt])[(int64_t)m * g.ldc[bt] + n] = (__bf16)y;
     } else {
         const int n = n0 + 4 * (l >> 4) + v;
         const float s = sum(idx);
         if (EPI == EPI_STORE_F32) {
-            static_cast<float *>(g.C[bt])[(int64_t)m * g.ldc + n] = s;
+            static_cast<float *>(g.C[bt])[(int64_t)m * g.ldc[bt] + n] = s;
         } else {
             const float b = g.bias[bt] ? (float)g.bias[bt][n] : 0.0f;
-            static_cast<__bf16 *>(g.C[bt])[(int64_t)m * g.ldc + n] = (__bf16)act<EPI>(s + b);
+            static_cast<__bf16 *>(g.C[bt])[(int64_t)m * g.ldc[bt] + n] = (__bf16)act<EPI>(s + b);
         }
     }
 }
@@ -269,12 +270,21 @@ hipError_t launch_ks(const GemvDev &g, int batch, hipStream_t s)
 }
 
 template <int EPI, int MT>
-hipError_t launch_mt(const GemvDev &g, int batch, hipStream_t s)
+hipError_t launch_mt(const GemvDev &g, int batch, int num_cu, hipStream_t s)
 {
     // Split K over the most waves (8 or 4) that still leaves each wave at
     // least 256 elements and an even number of 32-wide k-steps; K is a
     // multiple of 64, so a single wave always works.  Eight waves per block
-    // with two blocks per CU streamed faster than sixteen with one.
+    // with two blocks per CU streamed faster than sixteen with one.  A grid
+    // with fewer blocks than CUs (a narrow projection such as one rank's
+    // query, key or value block) has too few bytes in flight at eight
+    // waves: it takes sixteen, each wave with two 4 KiB units in flight.
+    const int blocks = g.N / (epi_gated(EPI) ? 8 : 16) * batch;
+    if (blocks < num_cu && (g.K / 16) % 128 == 0 && g.K / 16 >= 256) {
+        const dim3 grid((unsigned)(g.N / (epi_gated(EPI) ? 8 : 16)), (unsigned)batch);
+        hipLaunchKernelGGL((gemv_seg_kernel<EPI, MT, 16, 2>), grid, dim3(16 * 64), 0, s, g);
+        return hipGetLastError();
+    }
     if (g.K % (8 * 64) == 0 && g.K / 8 >= 256) return launch_ks<EPI, MT, 8>(g, batch, s);
     if (g.K % (4 * 64) == 0 && g.K / 4 >= 256) return launch_ks<EPI, MT, 4>(g, batch, s);
     return launch_ks<EPI, MT, 1>(g, batch, s);
@@ -282,7 +292,7 @@ hipError_t launch_mt(const GemvDev &g, int batch, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int /*num_cu*/, hipStream_t s)
+hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int num_cu, hipStream_t s)
 {
     GemvDev g;
     for (int b = 0; b < kMaxBatch; ++b) {
@@ -296,24 +306,24 @@ hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int /*num_cu*/, hip
     }
     g.ldx = a.lda;
     g.ldw = a.ldb;
-    g.ldc = a.ldc;
+    for (int b = 0; b < kMaxBatch; ++b) g.ldc[b] = ldc_of(a, b < a.batch ? b : 0);
     g.M = (int)a.M;
     g.N = (int)a.N;
     g.K = (int)a.K;
     const bool two = a.M > 16;
     switch (epi) {
     case EPI_BIAS_GELU:
-        return two ? launch_mt<EPI_BIAS_GELU, 2>(g, a.batch, s) : launch_mt<EPI_BIAS_GELU, 1>(g, a.batch, s);
+        return two ? launch_mt<EPI_BIAS_GELU, 2>(g, a.batch, num_cu, s) : launch_mt<EPI_BIAS_GELU, 1>(g, a.batch, num_cu, s);
     case EPI_STORE_F32:
-        return two ? launch_mt<EPI_STORE_F32, 2>(g, a.batch, s) : launch_mt<EPI_STORE_F32, 1>(g, a.batch, s);
+        return two ? launch_mt<EPI_STORE_F32, 2>(g, a.batch, num_cu, s) : launch_mt<EPI_STORE_F32, 1>(g, a.batch, num_cu, s);
     case EPI_BIAS_GELU_ERF:
-        return two ? launch_mt<EPI_BIAS_GELU_ERF, 2>(g, a.batch, s) : launch_mt<EPI_BIAS_GELU_ERF, 1>(g, a.batch, s);
+        return two ? launch_mt<EPI_BIAS_GELU_ERF, 2>(g, a.batch, num_cu, s) : launch_mt<EPI_BIAS_GELU_ERF, 1>(g, a.batch, num_cu, s);
     case EPI_GATED_TANH:
-        return two ? launch_mt<EPI_GATED_TANH, 2>(g, a.batch, s) : launch_mt<EPI_GATED_TANH, 1>(g, a.batch, s);
+        return two ? launch_mt<EPI_GATED_TANH, 2>(g, a.batch, num_cu, s) : launch_mt<EPI_GATED_TANH, 1>(g, a.batch, num_cu, s);
     case EPI_GATED_ERF:
-        return two ? launch_mt<EPI_GATED_ERF, 2>(g, a.batch, s) : launch_mt<EPI_GATED_ERF, 1>(g, a.batch, s);
+        return two ? launch_mt<EPI_GATED_ERF, 2>(g, a.batch, num_cu, s) : launch_mt<EPI_GATED_ERF, 1>(g, a.batch, num_cu, s);
     case EPI_BIAS:
-        return two ? launch_mt<EPI_BIAS, 2>(g, a.batch, s) : launch_mt<EPI_BIAS, 1>(g, a.batch, s);
+        return two ? launch_mt<EPI_BIAS, 2>(g, a.batch, num_cu, s) : launch_mt<EPI_BIAS, 1>(g, a.batch, num_cu, s);
     }
     return hipErrorInvalidValue;
 }

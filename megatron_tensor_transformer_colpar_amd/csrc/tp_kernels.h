@@ -37,9 +37,11 @@ struct GemmArgs {
     const void *bias2[kMaxBatch];  // gated epilogues: up bias [N] or nullptr
     void *C[kMaxBatch];
     int64_t ldc;
+    int64_t ldc_b[kMaxBatch];      // per-problem row stride of C; 0 = ldc
     int64_t M, N, K;
     int batch;
 };
+inline int64_t ldc_of(const GemmArgs &g, int b) { return g.ldc_b[b] ? g.ldc_b[b] : g.ldc; }
 
 // bf16 x bf16 -> fp32 accumulate, MFMA tiles; for M > 32.
 hipError_t launch_gemm_bf16(const GemmArgs &g, Epilogue epi, int num_cu, hipStream_t s);
@@ -70,7 +72,7 @@ struct AttnPlan {
     size_t ws_bytes;
 };
 AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv);
-hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnArgs &a, int num_cu, hipStream_t s);
 
 // out = (residual ? residual : 0) + sum_j partials[j]; optional bf16 copy,
 // optionally row-RMS-normalised.

@@ -62,14 +62,17 @@ def test_colpar_linear(M, H, N, T, dt, pad):
             assert bool((Y[:, Ns:] == 7.0).all()), "wrote outside the row's N/T columns"
 
 
-@pytest.mark.parametrize("M,nh,nkv,pad", [
-    (256, 8, 8, 0),     # one launch: Q, K and V as three problems of the same shape
-    (8, 8, 8, 0),       # skinny-M, one launch
-    (96, 8, 2, 0),      # grouped heads: K and V narrower, two launches
-    (8, 8, 4, 256),     # skinny-M, grouped, K/V rows strided as in a cache
+@pytest.mark.parametrize("M,H,nh,nkv,pad", [
+    (256, 512, 8, 8, 0),     # one launch: Q, K and V as three problems of the same shape
+    (8, 512, 8, 8, 0),       # skinny-M, one launch
+    (96, 512, 8, 2, 0),      # grouped heads: K and V narrower, two launches
+    (8, 512, 8, 4, 256),     # skinny-M, grouped, K/V rows strided as in a cache
+    (8, 8192, 16, 16, 1024), # the decode shape: 3 x 64 blocks < CUs, sixteen waves per
+                             # block; K/V strided as in a cache, still one launch
+    (32, 8192, 16, 16, 64),  # two token tiles, sixteen waves per block
 ])
-def test_qkv_colpar(M, nh, nkv, pad):
-    H, T = 512, 2
+def test_qkv_colpar(M, H, nh, nkv, pad):
+    T = 2
     A, Akv = nh * D, nkv * D
     X, Wq, Wk, Wv, bq, bk, bv = inputs.qkv_inputs(H, A, Akv, T, M=M, wid=61)
     i = 1

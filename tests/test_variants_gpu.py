@@ -163,3 +163,35 @@ def test_gated_mlp_shards_reduce_to_the_unsharded_block():
     print("  Z %.2e" % e)
     assert e <= TOL["bf16"]
     assert np.isfinite(to_f64(out)).all()
+
+
+# --------------------------------------- narrow grids (fewer blocks than CUs)
+@pytest.mark.parametrize("kind", ["gelu", "gated", "rowpar"])
+def test_narrow_skinny_grid_sixteen_waves(kind):
+    # K = 4096 and so few output columns that the skinny-M stream runs
+    # sixteen waves per block: every epilogue on that configuration
+    M, H = 8, 4096
+    if kind == "rowpar":
+        # Z [8, 1024] = Y [8, 4096] . W2 [4096, 1024]: 64 blocks, K = 4096
+        w = inputs.Workload(54, "narrow_rowpar", "bf16", M=M, H=1024, F=4096, T=1)
+        _, _, _, W2 = inputs.mlp_inputs(w, M=M)
+        Y = inputs.normal((M, 4096), 1.0, "bf16", seed=1, workload=54, tensor=inputs.X_ID)
+        Z = torch.empty(M, 1024, dtype=torch.float32, device="cuda")
+        tp.tp_rowpar_partial(Y.torch(), W2.transposed().torch(), Z, M, 1024, 4096, 1, 0, tp.TP_BF16)
+        torch.cuda.synchronize()
+        e = rel_fro(to_f64(Z), oracle.rowpar_partial(Y.f64, W2.f64, 1, 0))
+    elif kind == "gelu":
+        w = inputs.Workload(55, "narrow_gelu", "bf16", M=M, H=H, F=2048, T=2)
+        X, W1, b1, _ = inputs.mlp_inputs(w, M=M)
+        Y = torch.empty(M, 1024, dtype=torch.bfloat16, device="cuda")
+        tp.tp_colpar_act(X.torch(), W1.transposed().torch(), b1.torch(), Y, M, H, 2048, 2, 1, tp.TP_GELU_ERF)
+        torch.cuda.synchronize()
+        e = rel_fro(to_f64(Y), oracle.colpar_act(X.f64, W1.f64, b1.f64, 2, 1, ERF))
+    else:
+        w = inputs.Workload(56, "narrow_gated", "bf16", M=M, H=H, F=2048, T=2)
+        X, Wg, Wu, bg, bu = inputs.gated_inputs(w, M=M)
+        Y = run_gated(X, Wg, Wu, bg, bu, M, H, 2048, 2, 0, TANH, "bf16")
+        torch.cuda.synchronize()
+        e = rel_fro(to_f64(Y), oracle.colpar_gated(X.f64, Wg.f64, Wu.f64, bg.f64, bu.f64, 2, 0, TANH))
+    print("  %s %.2e" % (kind, e))
+    assert e <= TOL["bf16"]
