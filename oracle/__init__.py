@@ -58,9 +58,11 @@ def _bind(path):
     lib.orc_shard_reduce.argtypes = [i32, i64, i64, dp, dp, dp, dp, ctypes.c_double]
     lib.orc_mlp_unsharded.argtypes = [i64, i64, i64, dp, dp, dp, dp, dp, dp]
     lib.orc_attention.argtypes = [i64, i64, i64, i32, i32, i32, i32, dp, dp, dp, dp, dp]
+    lib.orc_act_grad.argtypes = [i32, i64, dp, dp]
+    lib.orc_mlp_shard_bwd.argtypes = [i64, i64, i64, i32, i32, i32] + [dp] * 12
     for f in (lib.orc_colpar_gelu, lib.orc_rowpar_partial, lib.orc_shard_reduce,
               lib.orc_mlp_unsharded, lib.orc_act, lib.orc_colpar_act, lib.orc_colpar_gated,
-              lib.orc_attention):
+              lib.orc_attention, lib.orc_act_grad, lib.orc_mlp_shard_bwd):
         f.restype = ctypes.c_int
     lib.orc_set_threads.argtypes = [i32]
     lib.orc_set_threads.restype = None
@@ -153,6 +155,41 @@ def colpar_act(X, W1, b1, T: int, i: int, form: int):
     Y = np.empty((M, F // T))
     _check(_load().orc_colpar_act(M, H, F, T, i, int(form), _p(X), _p(W1), _p(b1), _p(Y)), "colpar_act")
     return Y
+
+
+def act_grad(x, form: int):
+    """Derivative of either GeLU form (or of the identity), elementwise in fp64."""
+    x = _f64(x)
+    y = np.empty_like(x)
+    _check(_load().orc_act_grad(int(form), x.size, _p(x), _p(y)), "act_grad")
+    return y
+
+
+def mlp_shard_bwd(X, W1, b1, W2, dZ, T: int, i: int, form: int = ACT_GELU_TANH):
+    """Backward pass of rank i's MLP share for the output gradient dZ [M, H].
+
+    Returns a dict: dX_i [M,H] (a partial; dX = sum over ranks), dW1_i [H,Fs]
+    (columns C_i of dW1), db1_i [Fs], dW2_i [Fs,H] (rows C_i of dW2), and the
+    forward's U_i, Y_i and the GeLU-input gradient dU_i [M,Fs].
+    """
+    X = _f64(X)
+    M, H = X.shape
+    W1 = _f64(W1)
+    if W1.shape[0] != H:
+        raise ValueError("oracle: W1 must be [H, F]")
+    F = W1.shape[1]
+    W2 = _f64(W2, (F, H))
+    b1 = None if b1 is None else _f64(b1, (F,))
+    dZ = _f64(dZ, (M, H))
+    if F % T:
+        raise ValueError("oracle: F % T != 0")
+    Fs = F // T
+    out = {k: np.empty(s) for k, s in (("dX_i", (M, H)), ("dW1_i", (H, Fs)), ("db1_i", (Fs,)), ("dW2_i", (Fs, H)),
+                                       ("U_i", (M, Fs)), ("Y_i", (M, Fs)), ("dU_i", (M, Fs)))}
+    _check(_load().orc_mlp_shard_bwd(M, H, F, T, i, int(form), _p(X), _p(W1), _p(b1), _p(W2), _p(dZ),
+                                     _p(out["dX_i"]), _p(out["dW1_i"]), _p(out["db1_i"]), _p(out["dW2_i"]),
+                                     _p(out["U_i"]), _p(out["Y_i"]), _p(out["dU_i"])), "mlp_shard_bwd")
+    return out
 
 
 def colpar_linear(X, W, b, T: int, i: int):

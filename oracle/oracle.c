@@ -257,6 +257,108 @@ int orc_mlp_unsharded(int64_t M, int64_t H, int64_t F,
     return rc;
 }
 
+/* Derivative of either GeLU form ([GELU]):
+ *   tanh form: g(x) = x/2 (1 + tanh v), v = c (x + a x^3), c = sqrt(2/pi),
+ *              g'(x) = (1 + tanh v)/2 + x/2 (1 - tanh^2 v) c (1 + 3 a x^2);
+ *   exact form: g(x) = x Phi(x), g'(x) = Phi(x) + x phi(x),
+ *              phi(x) = exp(-x^2/2) / sqrt(2 pi). */
+static double act_grad(int32_t act, double x)
+{
+    if (act == ORC_ACT_NONE) return 1.0;
+    if (act == ORC_ACT_GELU_ERF) {
+        const double Phi = 0.5 * (1.0 + erf(x / sqrt(2.0)));
+        const double phi = exp(-0.5 * x * x) / sqrt(2.0 * acos(-1.0));
+        return Phi + x * phi;
+    }
+    const double c = sqrt(2.0 / acos(-1.0));
+    const double t = tanh(c * (x + 0.044715 * x * x * x));
+    return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * x * x);
+}
+
+int orc_act_grad(int32_t act, int64_t n, const double *x, double *y)
+{
+    if (!act_ok(act) || n < 0 || (n > 0 && (!x || !y))) return ORC_BAD_ARG;
+    for (int64_t k = 0; k < n; ++k) y[k] = act_grad(act, x[k]);
+    return ORC_OK;
+}
+
+/* Backward pass of rank i's MLP share, given dZ [M][H], the gradient of the
+ * loss at the block's output Z = sum_j Z_j.  The forward all-reduce hands
+ * every rank the same dZ, and the column-parallel input's gradient needs an
+ * all-reduce in the backward pass ([LESSON] forward and backward all-reduces
+ * on every layer; the column- and row-parallel layers' gradient contracts).
+ * With U_i = X W1[:, C_i] + b1[C_i], Y_i = g(U_i), Z_i = Y_i W2[C_i, :]:
+ *   dY_i        = dZ W2[C_i, :]^T               [M][Fs]
+ *   dU_i        = dY_i * g'(U_i)   (elementwise)
+ *   dX_i        = dU_i W1[:, C_i]^T             [M][H]   (a partial: dX = sum_i dX_i)
+ *   dW1[:, C_i] = X^T dU_i          -> dW1_i    [H][Fs]
+ *   db1[C_i]    = sum_m dU_i[m][:]  -> db1_i    [Fs]
+ *   dW2[C_i, :] = Y_i^T dZ          -> dW2_i    [Fs][H]
+ * Every sum runs in increasing index order.  Outputs U_i, Y_i, dU_i [M][Fs]
+ * may be NULL. */
+int orc_mlp_shard_bwd(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, int32_t act,
+                      const double *X, const double *W1, const double *b1, const double *W2,
+                      const double *dZ, double *dX_i, double *dW1_i, double *db1_i, double *dW2_i,
+                      double *U_out, double *Y_out, double *dU_out)
+{
+    if (!shard_ok(M, H, F, T, i) || !act_ok(act) || !X || !W1 || !W2 || !dZ || !dX_i || !dW1_i ||
+        !db1_i || !dW2_i)
+        return ORC_BAD_ARG;
+    const int64_t Fs = F / T, o = (int64_t)i * Fs;
+    const size_t n = (size_t)(M > 0 ? M : 1) * (size_t)Fs;
+    double *U = (double *)malloc(n * sizeof(double));
+    double *Y = (double *)malloc(n * sizeof(double));
+    double *dU = (double *)malloc(n * sizeof(double));
+    if (!U || !Y || !dU) {
+        free(U); free(Y); free(dU);
+        return ORC_BAD_ARG;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t c = 0; c < Fs; ++c) {
+            double u = 0.0;
+            for (int64_t h = 0; h < H; ++h) u += X[m * H + h] * W1[h * F + o + c];
+            if (b1) u += b1[o + c];
+            U[m * Fs + c] = u;
+            Y[m * Fs + c] = act_apply(act, u);
+            double dy = 0.0;
+            for (int64_t h = 0; h < H; ++h) dy += dZ[m * H + h] * W2[(o + c) * H + h];
+            dU[m * Fs + c] = dy * act_grad(act, u);
+        }
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t h = 0; h < H; ++h) {
+            double s = 0.0;
+            for (int64_t c = 0; c < Fs; ++c) s += dU[m * Fs + c] * W1[h * F + o + c];
+            dX_i[m * H + h] = s;
+        }
+    #pragma omp parallel for schedule(static)
+    for (int64_t h = 0; h < H; ++h)
+        for (int64_t c = 0; c < Fs; ++c) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; ++m) s += X[m * H + h] * dU[m * Fs + c];
+            dW1_i[h * Fs + c] = s;
+        }
+    for (int64_t c = 0; c < Fs; ++c) {
+        double s = 0.0;
+        for (int64_t m = 0; m < M; ++m) s += dU[m * Fs + c];
+        db1_i[c] = s;
+    }
+    #pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < Fs; ++c)
+        for (int64_t h = 0; h < H; ++h) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; ++m) s += Y[m * Fs + c] * dZ[m * H + h];
+            dW2_i[c * H + h] = s;
+        }
+    if (U_out) for (size_t k = 0; k < (size_t)M * (size_t)Fs; ++k) U_out[k] = U[k];
+    if (Y_out) for (size_t k = 0; k < (size_t)M * (size_t)Fs; ++k) Y_out[k] = Y[k];
+    if (dU_out) for (size_t k = 0; k < (size_t)M * (size_t)Fs; ++k) dU_out[k] = dU[k];
+    free(U); free(Y); free(dU);
+    return ORC_OK;
+}
+
 /* Scaled dot-product attention of one rank's heads ([ATTN] 3.2.1, 3.2.2;
  * [GUIDE] "Walking through a transformer block": a rank owns a block of
  * query heads, or of GQA groups, and the matching key/value heads, so the

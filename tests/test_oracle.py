@@ -337,7 +337,7 @@ def test_reduce_rms_closed_forms():
 
 def test_oracle_rejects_bad_arguments():
     with pytest.raises(ValueError):
-        oracle.act(np.ones(3), 2)                                         # unknown form
+        oracle.act(np.ones(3), 7)                                         # unknown form
     with pytest.raises(ValueError):
         oracle.colpar_gated(np.ones((2, 3)), np.ones((3, 4)), np.ones((3, 5)), None, None, 2, 0, ERF)
     with pytest.raises(ValueError):

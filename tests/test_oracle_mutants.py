@@ -3,8 +3,9 @@
 Each case compiles a copy of ``oracle/oracle.c`` with one plausible mistake (a
 dropped term, a wrong constant or sign, a missing shard offset, a missing bias,
 a skipped partial, swapped gate and up operands, swapped GeLU forms, a wrong
-attention scale, mask, head group or query position) and runs every pin of
-``test_oracle.py`` and ``test_oracle_attention.py`` against it; at
+attention scale, mask, head group or query position, a wrong GeLU derivative
+or gradient operand) and runs every pin of ``test_oracle.py``,
+``test_oracle_attention.py`` and ``test_oracle_backward.py`` against it; at
 least one pin has to fail.  Everything runs on the CPU.
 """
 import os
@@ -15,6 +16,7 @@ import pytest
 import oracle
 from tests import test_oracle as pins
 from tests import test_oracle_attention as attn_pins
+from tests import test_oracle_backward as bwd_pins
 
 MUTANTS = {
     "gelu_no_cubic": ("0.044715 * x * x * x", "0.0 * x"),
@@ -50,12 +52,21 @@ MUTANTS = {
     "attn_value_of_other_key": ("V + ((b * Lk + t) * nkv + g) * d", "V + ((b * Lk + (nkeys - 1 - t)) * nkv + g) * d"),
     "attn_queries_from_sequence_start": ("const int64_t p = len - Sq + s;", "const int64_t p = s;"),
     "attn_key_head_offset_dropped": ("K + ((b * Lk + t) * nkv + g) * d", "K + ((b * Lk + t) * nkv) * d"),
+    "bwd_tanh_grad_drops_second_term": ("return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * x * x);",
+                                        "return 0.5 * (1.0 + t);"),
+    "bwd_tanh_grad_cubic_coefficient": ("(1.0 + 3.0 * 0.044715 * x * x)", "(1.0 + 0.044715 * x * x)"),
+    "bwd_erf_grad_no_density_term": ("return Phi + x * phi;", "return Phi;"),
+    "bwd_dy_missing_shard_offset": ("dy += dZ[m * H + h] * W2[(o + c) * H + h];", "dy += dZ[m * H + h] * W2[c * H + h];"),
+    "bwd_dx_missing_shard_offset": ("s += dU[m * Fs + c] * W1[h * F + o + c];", "s += dU[m * Fs + c] * W1[h * F + c];"),
+    "bwd_dw1_uses_activation": ("s += X[m * H + h] * dU[m * Fs + c];", "s += X[m * H + h] * Y[m * Fs + c];"),
+    "bwd_db1_before_activation_grad": ("s += dU[m * Fs + c];", "s += dU[m * Fs + c] / act_grad(act, U[m * Fs + c]);"),
+    "bwd_dw2_uses_preactivation": ("s += Y[m * Fs + c] * dZ[m * H + h];", "s += U[m * Fs + c] * dZ[m * H + h];"),
 }
 
 
 def _all_pins():
     calls = []
-    for mod in (pins, attn_pins):
+    for mod in (pins, attn_pins, bwd_pins):
         for name in dir(mod):
             f = getattr(mod, name)
             if not name.startswith("test_") or not callable(f):
@@ -64,7 +75,14 @@ def _all_pins():
                 calls += [(name + "[T=%d]" % T, (lambda f=f, T=T: f(T))) for T in (1, 2, 4, 8)]
             elif name == "test_attn_head_shards_are_the_unsharded_heads":
                 calls += [(name + "[T=%d]" % T, (lambda f=f, T=T: f(T))) for T in (2, 4)]
-            elif name in ("test_oracle_rejects_bad_arguments", "test_attn_rejects_bad_arguments"):
+            elif name in ("test_backward_shards_reassemble_the_unsharded_gradients",
+                          "test_gelu_grad_is_the_derivative_of_gelu", "test_gelu_grad_odd_part_identity",
+                          "test_backward_matches_finite_differences"):
+                params = (2, 4) if name.startswith("test_backward_shards") else (oracle.ACT_GELU_TANH,
+                                                                                  oracle.ACT_GELU_ERF)
+                calls += [(name + "[%d]" % a, (lambda f=f, a=a: f(a))) for a in params]
+            elif name in ("test_oracle_rejects_bad_arguments", "test_attn_rejects_bad_arguments",
+                          "test_backward_rejects_bad_arguments"):
                 continue
             else:
                 calls.append((name, f))
