@@ -26,6 +26,9 @@ Also reported on the same JSON line:
                 prefill of 4 x 2048 tokens (Q/K/V projection, causal
                 attention, out-projection; TFLOP/s) and decode of M in
                 {1, 8, 32} sequences over 2048 cached positions (GB/s)
+  backward      rank 0's backward pass (training forward, dU with GeLU', dX,
+                dW1, dW2, db1) at the 2048-token block and 8192-token
+                prefill shapes (TFLOP/s; GB/s for db1)
   hipblaslt_context  the column-parallel launches next to torch.matmul
                 (hipBLASLt) on the same shapes, same GPU, same run
   cpu_baseline  the fp64 oracle on a bounded sample of the headline rows
@@ -369,6 +372,70 @@ def attention(args, torch, tp):
     return out
 
 
+def backward(args, torch, tp):
+    """The backward pass of rank 0's MLP share (bf16, fp32 gradients): the
+    training forward that keeps the GeLU input, then the input gradient fused
+    with GeLU' (dU), the input-gradient partial dX, the weight gradients dW1
+    and dW2 (each 2*M*H*F/T flops) and the bias gradient (a column sum,
+    HBM-bound), at the 2048-token block shape (H=4096, F/T=4096) and the
+    8192-token prefill shape (H=8192, F/T=4096).  An entry point called with
+    the other outputs NULL launches one kernel, so each is timed on its own;
+    dW2 is the whole row-parallel backward minus its dU launch."""
+    g = torch.Generator(device="cuda").manual_seed(13)
+    stream = torch.cuda.current_stream().cuda_stream
+    T1 = tp.TP_GELU_TANH
+    out = {}
+    for label, M, H, Fs in (("gpt_block_shard rank 0: M=2048 H=4096 F/T=4096", 2048, 4096, 4096),
+                            ("prefill rank 0: M=8192 H=8192 F/T=4096", 8192, 8192, 4096)):
+        def bf(*shape, std=1.0):
+            return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+        X, W1t, b1, W2t, dZ = bf(M, H), bf(Fs, H, std=0.02), bf(Fs, std=0.01), bf(H, Fs, std=0.02), bf(M, H)
+        Y, U, dU = (torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+        dX = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        dW1t = torch.empty(Fs, H, dtype=torch.float32, device="cuda")
+        db1 = torch.empty(Fs, dtype=torch.float32, device="cuda")
+        dW2t = torch.empty(H, Fs, dtype=torch.float32, device="cuda")
+        ops = [("forward_train", lambda: tp.tp_colpar_act_train(X, W1t, b1, Y, U, M, H, Fs, 1, 0, T1, stream)),
+               ("dU", lambda: tp.tp_rowpar_bwd(dZ, W2t, Y, U, dU, None, M, H, Fs, 1, 0, T1, 0, stream)),
+               ("dU+dW2", lambda: tp.tp_rowpar_bwd(dZ, W2t, Y, U, dU, dW2t, M, H, Fs, 1, 0, T1, 0, stream)),
+               ("dX", lambda: tp.tp_colpar_bwd(X, W1t, dU, dX, None, None, M, H, Fs, 1, 0, 0, stream)),
+               ("dW1", lambda: tp.tp_colpar_bwd(X, W1t, dU, None, dW1t, None, M, H, Fs, 1, 0, 0, stream)),
+               ("db1", lambda: tp.tp_colpar_bwd(X, W1t, dU, None, None, db1, M, H, Fs, 1, 0, 0, stream)),
+               ("backward", lambda: tp.tp_mlp_shard_bwd(X, W1t, W2t, U, Y, dZ, dU, dX, dW1t, db1, dW2t, M, H, Fs, 1,
+                                                        0, T1, 0, stream))]
+        ms = {}
+        n = max(3, args.steps // 5)
+        for name, f in ops:
+            for _ in range(2):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(n):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            ms[name] = e0.elapsed_time(e1) / n
+        ms["dW2"] = ms.pop("dU+dW2") - ms["dU"]
+        fl = 2.0 * M * H * Fs
+        e = {}
+        for name in ("forward_train", "dU", "dX", "dW1", "dW2"):
+            t = fl / (ms[name] * 1e-3) / 1e12
+            e[name] = {"us": round(ms[name] * 1e3, 2), "tflops": round(t, 1), "frac": round(t / PEAK_BF16_TFLOPS, 4)}
+        e["dW2"]["derived"] = "row-parallel backward minus its dU launch"
+        by = M * Fs * 2 + Fs * 4
+        e["db1"] = {"us": round(ms["db1"] * 1e3, 2), "gbs": round(by / (ms["db1"] * 1e-3) / 1e9, 1),
+                    "frac": round(by / (ms["db1"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        t = 4 * fl / (ms["backward"] * 1e-3) / 1e12
+        e["backward"] = {"us": round(ms["backward"] * 1e3, 2), "tflops": round(t, 1),
+                         "frac": round(t / PEAK_BF16_TFLOPS, 4)}
+        out[label] = e
+        log("[bench] backward %s: %s" % (label, e))
+        del X, W1t, b1, W2t, dZ, Y, U, dU, dX, dW1t, db1, dW2t
+        torch.cuda.empty_cache()
+    return out
+
+
 def hipblaslt_context(args, torch, tp):
     """The library's column-parallel launches next to hipBLASLt (torch.matmul,
     bf16 out, no bias or GeLU) on the same shapes, timed alternately on the
@@ -579,7 +646,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline step only (for profiling)")
-    ap.add_argument("--sections", default="prefill,decode,stack80,variants,attention,context",
+    ap.add_argument("--sections", default="prefill,decode,stack80,variants,attention,backward,context",
                     help="comma-separated extra sections to run after the headline step")
     ap.add_argument("--context-only", action="store_true",
                     help="only the library-vs-hipBLASLt comparison (for counter runs)")
@@ -639,6 +706,8 @@ def main():
     if "attention" in sections:
         rec["attention"] = attention(args, torch, tp)
         torch.cuda.empty_cache()
+    if "backward" in sections:
+        rec["backward"] = backward(args, torch, tp)
     if "context" in sections:
         rec["hipblaslt_context"] = hipblaslt_context(args, torch, tp)
     if not args.no_cpu_baseline:

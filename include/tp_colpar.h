@@ -332,6 +332,73 @@ tp_status tp_attn_core(const void *Q, const void *K, const void *V, void *ctx, c
  * the sizes only, not on the device. */
 size_t tp_attn_workspace_bytes(int64_t Bs, int64_t Sq, int64_t Lk, int32_t nh, int32_t nkv);
 
+/*
+ * ---- Backward pass of rank i's share (bf16; gradients in fp32) ----
+ * [LESSON] forward and backward all-reduces on every layer: the forward's
+ * All-Reduce-Sum gives every rank the same output gradient dZ, and the
+ * column-parallel layer's input gradient is a partial sum that the backward
+ * all-reduce completes (on one GPU: tp_shard_reduce over the ranks' dX_i);
+ * the weight and bias gradients of a rank are its own blocks, with no
+ * communication.  With U_i = X W1[:,C_i] + b1[C_i] (the GeLU input) and
+ * Y_i = g(U_i):
+ *   dU_i        = (dZ W2[C_i,:]^T) * g'(U_i)
+ *   dX_i        = dU_i W1[:,C_i]^T            (partial; dX = sum_i dX_i)
+ *   dW1[:,C_i]  = X^T dU_i,   db1[C_i] = sum over tokens of dU_i
+ *   dW2[C_i,:]  = Y_i^T dZ
+ * Gradients are stored like the weights (dW1t = dW1^T [F][H], dW2t = dW2^T
+ * [H][F], db1 [F], all fp32); rank i writes only its blocks.  With
+ * TP_GRAD_ACCUMULATE they are added to the buffers' contents instead
+ * (gradient accumulation over micro-batches).  M == 0 enqueues nothing and
+ * writes nothing.  Validation: the forward's shape checks (F % T, H and F/T
+ * multiples of 64, ...) plus (max(M, H, F/T) + 64) * max(H, F) < 2^30
+ * (TP_ERR_UNSUPPORTED), unknown flags (TP_ERR_UNSUPPORTED), outputs
+ * overlapping inputs or each other (TP_ERR_ALIAS).
+ */
+#define TP_GRAD_ACCUMULATE 1u
+
+/*
+ * Training forward of the column-parallel up-projection: tp_colpar_act in
+ * bf16, and the GeLU input U_i [M][F/T] (bf16) is kept for the backward.
+ */
+tp_status tp_colpar_act_train(const void *X, const void *W1t, const void *b1, void *Y_i, void *U_i,
+                              int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, tp_act act,
+                              hipStream_t stream);
+
+/*
+ * Backward of rank i's row-parallel projection (A3; the head-sharded
+ * out-projection A4 with F := A and U_i = NULL):
+ *   dU_i [M][F/T] bf16 = (dZ . W2[C_i,:]^T) * g'(U_i), or without U_i the
+ *                        plain input gradient dZ . W2[C_i,:]^T
+ *   dW2t columns C_i   = (Y_i^T . dZ)^T  (fp32, written or accumulated);
+ *                        dW2t may be NULL (then Y_i may be NULL too)
+ *   dZ [M][H] bf16, W2t [H][F] bf16, Y_i and U_i [M][F/T] bf16.
+ */
+tp_status tp_rowpar_bwd(const void *dZ, const void *W2t, const void *Y_i, const void *U_i, void *dU_i,
+                        float *dW2t, int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, tp_act act,
+                        uint32_t flags, hipStream_t stream);
+
+/*
+ * Backward of rank i's column-parallel projection (A1+A2), from the
+ * gradient at its output dU_i [M][F/T] bf16 (the GeLU input's, from
+ * tp_rowpar_bwd):
+ *   dX_i [M][H] fp32 = dU_i . W1[:,C_i]^T          (may be NULL)
+ *   dW1t rows C_i    = (X^T . dU_i)^T, fp32 [F][H]  (may be NULL)
+ *   db1[C_i]         = column sums of dU_i, fp32 [F] (may be NULL)
+ */
+tp_status tp_colpar_bwd(const void *X, const void *W1t, const void *dU_i, float *dX_i, float *dW1t,
+                        float *db1, int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, uint32_t flags,
+                        hipStream_t stream);
+
+/*
+ * Rank i's whole backward: tp_rowpar_bwd into the caller's workspace dU_ws
+ * [M][F/T] bf16, then tp_colpar_bwd from it.  U_i and Y_i come from
+ * tp_colpar_act_train.
+ */
+tp_status tp_mlp_shard_bwd(const void *X, const void *W1t, const void *W2t, const void *U_i, const void *Y_i,
+                           const void *dZ, void *dU_ws, float *dX_i, float *dW1t, float *db1, float *dW2t,
+                           int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, tp_act act, uint32_t flags,
+                           hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *tp_last_error(void);
 

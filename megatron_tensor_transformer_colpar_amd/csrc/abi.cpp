@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdint>
+#include <algorithm>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -293,6 +294,43 @@ tp_status validate_linear(const char *fn, const void *X, const void *Wt, const v
     if (overlap(y, span(X, M * H * es)) || overlap(y, span(Wt, N * H * es)) || (b && overlap(y, span(b, N * es))))
         return fail(TP_ERR_ALIAS, "%s: an output overlaps an input", fn);
     return TP_OK;
+}
+
+// ---- backward pass ----
+// Shapes of the bf16 backward entry points: the forward's checks, plus the
+// 32-bit byte offsets of the operands read along K (k-rows of up to
+// max(H, F) elements, K up to max(M, H, F/T), padded by one 64-row slice).
+tp_status check_bwd(const char *fn, int64_t M, int64_t H, int64_t F, int32_t T, int32_t i)
+{
+    tp_status st = check_shard(fn, M, H, F, T, i, TP_BF16);
+    if (st != TP_OK) return st;
+    if ((st = check_dims64(fn, H, F, T)) != TP_OK) return st;
+    const int64_t kmax = std::max(M, std::max(H, F / T)), ldmax = std::max(H, F);
+    if ((kmax + 64) * ldmax * 2 >= (int64_t(1) << 31))
+        return fail(TP_ERR_UNSUPPORTED, "%s: M, H or F too large for the kernels' 32-bit offsets", fn);
+    return TP_OK;
+}
+
+// Every output range against every input range and every other output
+// (nullptr entries are skipped).
+tp_status check_disjoint(const char *fn, const Range *out, int nout, const Range *in, int nin)
+{
+    for (int a = 0; a < nout; ++a) {
+        if (out[a].lo == out[a].hi) continue;
+        for (int b = 0; b < nin; ++b)
+            if (overlap(out[a], in[b])) return fail(TP_ERR_ALIAS, "%s: an output overlaps an input", fn);
+        for (int b = a + 1; b < nout; ++b)
+            if (overlap(out[a], out[b])) return fail(TP_ERR_ALIAS, "%s: two outputs overlap", fn);
+    }
+    return TP_OK;
+}
+
+Range span_or_none(const void *p, int64_t bytes) { return p ? span(p, bytes) : Range{0, 0}; }
+
+hipError_t launch_mfma(tpk::GemmArgs g, tpk::Epilogue epi, tpk::Layout lay, hipStream_t s)
+{
+    g.layout = lay;
+    return tpk::launch_gemm_bf16(g, epi, num_cu(), s);
 }
 
 constexpr int64_t kAttnMaxRowBytes = int64_t(1) << 31;   // per sequence, padded rows included
@@ -609,6 +647,171 @@ size_t tp_attn_workspace_bytes(int64_t Bs, int64_t Sq, int64_t Lk, int32_t nh, i
     if (Bs < 1 || Sq < 1 || Lk < 1 || nh < 1 || nkv < 1 || nh % nkv != 0) return 0;
     const tpk::AttnPlan p = tpk::attn_plan(Bs, Sq, Lk, nh, nkv);
     return p.decode ? p.ws_bytes : 0;
+}
+
+tp_status tp_colpar_act_train(const void *X, const void *W1t, const void *b1, void *Y_i, void *U_i, int64_t M,
+                              int64_t H, int64_t F, int32_t T, int32_t i, tp_act act, hipStream_t stream)
+{
+    const char *fn = "tp_colpar_act_train";
+    tp_status st = validate_colpar(fn, X, W1t, b1, Y_i, M, H, F, T, i, TP_BF16);
+    if (st != TP_OK) return st;
+    if ((st = check_act(fn, act)) != TP_OK) return st;
+    if (!U_i) return fail(TP_ERR_NULL, "%s: U_i must be non-NULL", fn);
+    if (!aligned16(U_i)) return fail(TP_ERR_UNSUPPORTED, "%s: U_i must be 16-byte aligned", fn);
+    const int64_t Fs = F / T;
+    if (M > 0) {
+        const Range u = span(U_i, M * Fs * 2);
+        const Range in[4] = {span(X, M * H * 2), span(W1t, F * H * 2), span_or_none(b1, F * 2), span(Y_i, M * Fs * 2)};
+        for (const Range &r : in)
+            if (overlap(u, r)) return fail(TP_ERR_ALIAS, "%s: U_i overlaps another buffer", fn);
+    }
+    if (M == 0) return ok();
+    tpk::GemmArgs g = colpar_args(X, W1t, b1, &Y_i, 1, i, M, H, F, T, TP_BF16);
+    g.aux[0] = U_i;
+    g.ldaux = Fs;
+    // the GeLU input is kept by the MFMA GEMM's epilogue at every M
+    const hipError_t e =
+        launch_mfma(g, act == TP_GELU_ERF ? tpk::EPI_BIAS_GELU_ERF : tpk::EPI_BIAS_GELU, tpk::LAYOUT_KCONTIG, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "training column-parallel launch");
+}
+
+tp_status tp_rowpar_bwd(const void *dZ, const void *W2t, const void *Y_i, const void *U_i, void *dU_i, float *dW2t,
+                        int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, tp_act act, uint32_t flags,
+                        hipStream_t stream)
+{
+    const char *fn = "tp_rowpar_bwd";
+    tp_status st = check_bwd(fn, M, H, F, T, i);
+    if (st != TP_OK) return st;
+    if (!dZ || !W2t || !dU_i) return fail(TP_ERR_NULL, "%s: dZ, W2t and dU_i must be non-NULL", fn);
+    if (dW2t && !Y_i) return fail(TP_ERR_NULL, "%s: the weight gradient needs Y_i", fn);
+    if (U_i && (st = check_act(fn, act)) != TP_OK) return st;
+    if (flags & ~TP_GRAD_ACCUMULATE) return fail(TP_ERR_UNSUPPORTED, "%s: unknown flags 0x%x", fn, flags);
+    if (!aligned16(dZ) || !aligned16(W2t) || !aligned16(dU_i) || (Y_i && !aligned16(Y_i)) ||
+        (U_i && !aligned16(U_i)) || (dW2t && !aligned16(dW2t)))
+        return fail(TP_ERR_UNSUPPORTED, "%s: every buffer must be 16-byte aligned", fn);
+    const int64_t Fs = F / T;
+    if (M > 0) {
+        const Range out[2] = {span(dU_i, M * Fs * 2), span_or_none(dW2t, H * F * 4)};
+        const Range in[4] = {span(dZ, M * H * 2), span(W2t, H * F * 2), span_or_none(Y_i, M * Fs * 2),
+                             span_or_none(U_i, M * Fs * 2)};
+        if ((st = check_disjoint(fn, out, 2, in, 4)) != TP_OK) return st;
+    }
+    if (M == 0) return ok();
+    // dY_i = dZ . W2[C_i,:]^T (B = columns C_i of W2^T, read along H), times g'(U_i)
+    tpk::GemmArgs g = empty_args();
+    g.A[0] = dZ;
+    g.lda = H;
+    g.B[0] = static_cast<const char *>(W2t) + (int64_t)i * Fs * 2;
+    g.ldb = F;
+    g.C[0] = dU_i;
+    g.ldc = Fs;
+    g.aux[0] = const_cast<void *>(U_i);
+    g.ldaux = Fs;
+    g.M = M;
+    g.N = Fs;
+    g.K = H;
+    const tpk::Epilogue e1 = !U_i ? tpk::EPI_BIAS : act == TP_GELU_ERF ? tpk::EPI_GELU_GRAD_ERF : tpk::EPI_GELU_GRAD_TANH;
+    hipError_t e = launch_mfma(g, e1, tpk::LAYOUT_B_KMAJOR, stream);
+    if (e != hipSuccess) return hip_fail(e, "row-parallel input-gradient launch");
+    if (!dW2t) return ok();
+    // dW2[C_i,:] = Y_i^T . dZ, stored as columns C_i of dW2^T: C[h][f] = sum_m dZ[m][h] Y_i[m][f]
+    tpk::GemmArgs w = empty_args();
+    w.A[0] = dZ;
+    w.lda = H;
+    w.B[0] = Y_i;
+    w.ldb = Fs;
+    w.C[0] = dW2t + (int64_t)i * Fs;
+    w.ldc = F;
+    w.M = H;
+    w.N = Fs;
+    w.K = M;
+    e = launch_mfma(w, (flags & TP_GRAD_ACCUMULATE) ? tpk::EPI_ACC_F32 : tpk::EPI_STORE_F32, tpk::LAYOUT_AB_KMAJOR,
+                    stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "row-parallel weight-gradient launch");
+}
+
+tp_status tp_colpar_bwd(const void *X, const void *W1t, const void *dU_i, float *dX_i, float *dW1t, float *db1,
+                        int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, uint32_t flags, hipStream_t stream)
+{
+    const char *fn = "tp_colpar_bwd";
+    tp_status st = check_bwd(fn, M, H, F, T, i);
+    if (st != TP_OK) return st;
+    if (!dU_i || (dX_i && !W1t) || (dW1t && !X))
+        return fail(TP_ERR_NULL, "%s: dU_i, and the inputs of each requested gradient, must be non-NULL", fn);
+    if (flags & ~TP_GRAD_ACCUMULATE) return fail(TP_ERR_UNSUPPORTED, "%s: unknown flags 0x%x", fn, flags);
+    if (!aligned16(dU_i) || (X && !aligned16(X)) || (W1t && !aligned16(W1t)) || (dX_i && !aligned16(dX_i)) ||
+        (dW1t && !aligned16(dW1t)) || (db1 && !aligned16(db1)))
+        return fail(TP_ERR_UNSUPPORTED, "%s: every buffer must be 16-byte aligned", fn);
+    const int64_t Fs = F / T;
+    if (M > 0) {
+        const Range out[3] = {span_or_none(dX_i, M * H * 4), span_or_none(dW1t, F * H * 4), span_or_none(db1, F * 4)};
+        const Range in[3] = {span_or_none(X, M * H * 2), span_or_none(W1t, F * H * 2), span(dU_i, M * Fs * 2)};
+        if ((st = check_disjoint(fn, out, 3, in, 3)) != TP_OK) return st;
+    }
+    if (M == 0) return ok();
+    const bool acc = flags & TP_GRAD_ACCUMULATE;
+    hipError_t e;
+    if (dX_i) {
+        // dX_i = dU_i . W1[:,C_i]^T (B = rows C_i of W1^T, read along F/T): a partial over ranks
+        tpk::GemmArgs g = empty_args();
+        g.A[0] = dU_i;
+        g.lda = Fs;
+        g.B[0] = static_cast<const char *>(W1t) + (int64_t)i * Fs * H * 2;
+        g.ldb = H;
+        g.C[0] = dX_i;
+        g.ldc = H;
+        g.M = M;
+        g.N = H;
+        g.K = Fs;
+        if ((e = launch_mfma(g, tpk::EPI_STORE_F32, tpk::LAYOUT_B_KMAJOR, stream)) != hipSuccess)
+            return hip_fail(e, "column-parallel input-gradient launch");
+    }
+    if (dW1t) {
+        // dW1[:,C_i] = X^T . dU_i, stored as rows C_i of dW1^T: C[f][h] = sum_m dU_i[m][f] X[m][h]
+        tpk::GemmArgs w = empty_args();
+        w.A[0] = dU_i;
+        w.lda = Fs;
+        w.B[0] = X;
+        w.ldb = H;
+        w.C[0] = dW1t + (int64_t)i * Fs * H;
+        w.ldc = H;
+        w.M = Fs;
+        w.N = H;
+        w.K = M;
+        if ((e = launch_mfma(w, acc ? tpk::EPI_ACC_F32 : tpk::EPI_STORE_F32, tpk::LAYOUT_AB_KMAJOR, stream)) !=
+            hipSuccess)
+            return hip_fail(e, "column-parallel weight-gradient launch");
+    }
+    if (db1 && (e = tpk::launch_colsum_bf16(dU_i, Fs, M, Fs, db1 + (int64_t)i * Fs, acc, stream)) != hipSuccess)
+        return hip_fail(e, "bias-gradient launch");
+    return ok();
+}
+
+tp_status tp_mlp_shard_bwd(const void *X, const void *W1t, const void *W2t, const void *U_i, const void *Y_i,
+                           const void *dZ, void *dU_ws, float *dX_i, float *dW1t, float *db1, float *dW2t, int64_t M,
+                           int64_t H, int64_t F, int32_t T, int32_t i, tp_act act, uint32_t flags, hipStream_t stream)
+{
+    const char *fn = "tp_mlp_shard_bwd";
+    if (!U_i) return fail(TP_ERR_NULL, "%s: U_i must be non-NULL", fn);
+    tp_status st = check_bwd(fn, M, H, F, T, i);
+    if (st != TP_OK) return st;
+    if (M > 0 && dU_ws) {
+        const int64_t Fs = F / T;
+        const Range ws = span(dU_ws, M * Fs * 2);
+        const Range others[5] = {span_or_none(X, M * H * 2), span_or_none(W1t, F * H * 2), span_or_none(dX_i, M * H * 4),
+                                 span_or_none(dW1t, F * H * 4), span_or_none(db1, F * 4)};
+        for (const Range &r : others)
+            if (overlap(ws, r)) return fail(TP_ERR_ALIAS, "%s: dU_ws overlaps another buffer", fn);
+    }
+    if ((st = tp_rowpar_bwd(dZ, W2t, Y_i, U_i, dU_ws, dW2t, M, H, F, T, i, act, flags, stream)) != TP_OK) {
+        g_err = std::string(fn) + ": " + g_err;
+        return st;
+    }
+    if ((st = tp_colpar_bwd(X, W1t, dU_ws, dX_i, dW1t, db1, M, H, F, T, i, flags, stream)) != TP_OK) {
+        g_err = std::string(fn) + ": " + g_err;
+        return st;
+    }
+    return ok();
 }
 
 const char *tp_last_error(void) { return g_err.c_str(); }

@@ -48,6 +48,29 @@ __device__ __forceinline__ float gelu_erf(float x)
     return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
 }
 
+// GeLU derivatives ([GELU]).  Tanh form: with s = (1 + tanh v)/2 =
+// 1/(1 + e^(-2v)), v = c(x + a x^3), g'(x) = s + 2 x s (1 - s) c (1 + 3 a x^2).
+// Exact form: g'(x) = Phi(x) + x phi(x).
+__device__ __forceinline__ float gelu_tanh_grad(float x)
+{
+    constexpr float c = 0.7978845608028654f, a = 0.044715f;
+    const float s = __fdividef(1.0f, 1.0f + __expf(-2.0f * c * x * (1.0f + a * x * x)));
+    return s + 2.0f * x * s * (1.0f - s) * c * (1.0f + 3.0f * a * x * x);
+}
+__device__ __forceinline__ float gelu_erf_grad(float x)
+{
+    return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.3989422804014327f * __expf(-0.5f * x * x);
+}
+
+template <int EPI>
+__device__ __forceinline__ float act_grad(float x)
+{
+    if constexpr (EPI == EPI_GELU_GRAD_ERF)
+        return gelu_erf_grad(x);
+    else
+        return gelu_tanh_grad(x);
+}
+
 // The activation an epilogue applies.
 template <int EPI>
 __device__ __forceinline__ float act(float x)

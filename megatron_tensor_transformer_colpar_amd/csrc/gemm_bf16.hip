@@ -37,7 +37,9 @@ struct GemmDev {
     const __bf16 *bias[kMaxBatch];
     const __bf16 *B2[kMaxBatch];     // gated epilogues: up rows
     const __bf16 *bias2[kMaxBatch];  // gated epilogues: up bias
+    __bf16 *aux[kMaxBatch];          // GeLU input: read by the gradient epilogues, written by the GeLU ones
     void *C[kMaxBatch];
+    int64_t ldaux;
     int64_t lda, ldb;
     int64_t ldc[kMaxBatch];
     int M, N, K;
@@ -45,6 +47,10 @@ struct GemmDev {
 };
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
+typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4v;
+typedef __attribute__((address_space(3))) char lds_char;
 
 // LDS rows hold BK bf16 = CH chunks of 16 B; chunk c of row r sits at slot
 // c ^ swz(r).  The two swizzles make every ds_read_b128 of a fragment (32
@@ -81,11 +87,25 @@ struct Cfg {
     static_assert((S - 2) * LOADS <= 63, "vmcnt range");
 };
 
-template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI>
+// Operand layouts.  K-contiguous (the forward's weights and activations):
+// row r of an operand holds its K values, and a tile is BM (or BN) rows of
+// BK values.  K-major (LAY 1: B; LAY 2: A and B): element (r, k) sits at
+// k * ld + r, as for an activation read along its token axis (the weight
+// gradients) or a K-contiguous weight read along its output axis (the input
+// gradients).  A K-major tile is BK rows (k) of BM (or BN) values; chunk c
+// of k-row kr sits at slot c ^ 4(kr & 3), and an MFMA fragment (8 k values
+// of one r) is two LDS transpose reads (ds_read_b64_tr_b16: in a 16-lane
+// group, lane i gets element i%4 of the 8-byte rows addressed by lanes
+// 4j + i/4); the 4 k-rows x 64 bytes a half-wave reads then cover all 64
+// banks once.  A K-major operand's k-rows are range-checked like rows, so
+// K need not be a multiple of BK.
+template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY>
 __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 {
     using C_ = Cfg<BM, BN, BK, S, NW>;
     constexpr int TM = C_::TM, TN = C_::TN, STAGE = C_::STAGE, CH = C_::CH, RB = C_::RB, KQ = C_::KQ;
+    constexpr bool AKM = LAY == 2, BKM = LAY >= 1;   // K-major operands
+    static_assert(!(AKM || BKM) || (BK == 64 && BM >= 128 && BN >= 128 && NW % 2 == 0), "K-major tile shape");
     // Gated: each wave's WTN rows of the B tile are WTN/2 gate rows followed
     // by the matching WTN/2 up rows, so accumulator tiles j and j + TN/2 of a
     // lane hold gate and up of the same output elements; a tile then covers
@@ -113,12 +133,17 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     const __bf16 *const bias_p = g.bias[bt];
     void *const Cbase = g.C[bt];
     const int64_t ldc = g.ldc[bt];
+    __bf16 *const aux_p = g.aux[bt];
 
     const int a_rows = min(BM, g.M - m0), b_rows = min(BNO, g.N - n0);
+    // K-contiguous: the tile's rows; K-major: the tile's columns onward, the
+    // range ending after the K-th k-row (later k-rows read as zero)
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(Abase + (int64_t)m0 * g.lda, (uint32_t)((int64_t)a_rows * g.lda * 2));
+        make_rsrc(AKM ? Abase + m0 : Abase + (int64_t)m0 * g.lda,
+                  (uint32_t)(AKM ? ((int64_t)g.K * g.lda - m0) * 2 : (int64_t)a_rows * g.lda * 2));
     const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(Bbase + (int64_t)n0 * g.ldb, (uint32_t)((int64_t)b_rows * g.ldb * 2));
+        make_rsrc(BKM ? Bbase + n0 : Bbase + (int64_t)n0 * g.ldb,
+                  (uint32_t)(BKM ? ((int64_t)g.K * g.ldb - n0) * 2 : (int64_t)b_rows * g.ldb * 2));
     // (resources are only ever built from pointers: a conditional expression
     // of resource type makes the host compilation drop the kernel's stub)
     const __amdgpu_buffer_rsrc_t rb2 =
@@ -134,7 +159,16 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     const uint32_t a_voff = (uint32_t)(drow * g.lda * 2 + dchunk * 16);
     const uint32_t b_voff = (uint32_t)(drow * g.ldb * 2 + dchunk * 16);
     const uint32_t a_jstep = (uint32_t)(NW * RB * g.lda * 2), b_jstep = (uint32_t)(NW * RB * g.ldb * 2);
-    const int KT = g.K / BK;
+    // K-major tiles: a 1 KiB block is KRA (KRB) k-rows of BM/8 (BN/8)
+    // chunks; instruction j of wave w fills block NW*j + w, lane L lands in
+    // k-row L/(BM/8) of it, physical chunk L%(BM/8), and fetches the logical
+    // chunk the swizzle puts there (k-row & 3 does not depend on j).
+    constexpr int ACH = BM / 8, BCH = BN / 8, KRA = 64 / ACH, KRB = 64 / BCH;
+    const int a_krow = wave * KRA + lane / ACH, b_krow = wave * KRB + lane / BCH;
+    const uint32_t ak_voff = (uint32_t)((a_krow * g.lda + 8 * ((lane % ACH) ^ (4 * (a_krow & 3)))) * 2);
+    const uint32_t bk_voff = (uint32_t)((b_krow * g.ldb + 8 * ((lane % BCH) ^ (4 * (b_krow & 3)))) * 2);
+    const uint32_t ak_jstep = (uint32_t)(NW * KRA * g.lda * 2), bk_jstep = (uint32_t)(NW * KRB * g.ldb * 2);
+    const int KT = (AKM || BKM) ? (g.K + BK - 1) / BK : g.K / BK;
     // Gated B rows: instruction j of this wave fills tile rows r0 .. r0+RB-1,
     // r0 = RB(NW*j + wave), all in one half of one wave's WTN rows; they come
     // from output rows ob .. ob+RB-1 of the gate (first half) or up matrix.
@@ -154,12 +188,21 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     auto issue = [&](u32x4 *stage, int kt) __attribute__((always_inline)) {
         const uint32_t koff = (uint32_t)min(kt, KT - 1) * (BK * 2);
 #pragma unroll
-        for (int j = 0; j < C_::A_LD; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(stage + (NW * j + wave) * 64), 16,
-                                                    a_voff + j * a_jstep, koff, 0, 0);
+        for (int j = 0; j < C_::A_LD; ++j) {
+            if constexpr (AKM) {
+                const uint32_t vo = ak_voff + j * ak_jstep + (uint32_t)min(kt, KT - 1) * (uint32_t)(BK * g.lda * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(stage + (NW * j + wave) * 64), 16, vo, 0, 0, 0);
+            } else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(stage + (NW * j + wave) * 64), 16,
+                                                        a_voff + j * a_jstep, koff, 0, 0);
+        }
 #pragma unroll
         for (int j = 0; j < C_::B_LD; ++j) {
-            if constexpr (GATED) {
+            if constexpr (BKM) {
+                const uint32_t vo = bk_voff + j * bk_jstep + (uint32_t)min(kt, KT - 1) * (uint32_t)(BK * g.ldb * 2);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16, vo,
+                                                        0, 0, 0);
+            } else if constexpr (GATED) {
                 // the offset goes through a local: an array element passed
                 // straight to the builtin also makes the host pass drop the stub
                 const uint32_t vo = gv_off[j];
@@ -181,15 +224,41 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     const int a_base = (wm * C_::WTM + frow) * CH;
     const int b_base = (BM + wn * C_::WTN + frow) * CH;
 
+    // K-major fragment of 32-row block rb (r = rb + lane%32), k-step q: the
+    // transpose read e4 gives k = 16q + 8*fhalf + 4*e4 + 0..3; the addressing
+    // lane (i = lane%16) names k-row +i/4, 8 bytes at r = rb + 16*((lane/16)%2) + 4*(i%4).
+    const int trr = (lane >> 2) & 3;
+    const int tr_lane = 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
+    int a_tr[TM], b_tr[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a_tr[i] = 16 * (((wm * C_::WTM + 32 * i) / 8) ^ (4 * trr)) + tr_lane;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b_tr[j] = 16 * (((wn * C_::WTN + 32 * j) / 8) ^ (4 * trr)) + tr_lane;
+    auto tr_frag = [&](const u32x4 *region, int rowbytes, int off, int q) __attribute__((always_inline)) {
+        const lds_char *base = reinterpret_cast<const lds_char *>(LDS_PTR(region));
+        const int k0 = 16 * q + 8 * fhalf + trr;
+        const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(base + k0 * rowbytes + off));
+        const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(base + (k0 + 4) * rowbytes + off));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+
     bf16x8 fa[2][TM], fb[2][TN];
     auto read_frags = [&](const u32x4 *stage, int q, int p) __attribute__((always_inline)) {
         const int slot = (2 * q + fhalf) ^ fsw;
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-            fa[p][i] = __builtin_bit_cast(bf16x8, stage[a_base + i * 32 * CH + slot]);
+        for (int i = 0; i < TM; ++i) {
+            if constexpr (AKM)
+                fa[p][i] = tr_frag(stage, BM * 2, a_tr[i], q);
+            else
+                fa[p][i] = __builtin_bit_cast(bf16x8, stage[a_base + i * 32 * CH + slot]);
+        }
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-            fb[p][j] = __builtin_bit_cast(bf16x8, stage[b_base + j * 32 * CH + slot]);
+        for (int j = 0; j < TN; ++j) {
+            if constexpr (BKM)
+                fb[p][j] = tr_frag(stage + BM * CH, BN * 2, b_tr[j], q);
+            else
+                fb[p][j] = __builtin_bit_cast(bf16x8, stage[b_base + j * 32 * CH + slot]);
+        }
     };
 
     f32x16 acc[TM][TN];
@@ -333,7 +402,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
             const int nb = n0 + wn * C_::WTN + j * 32 + 4 * fhalf;
             f32x4 bias[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bias[q] = EPI == EPI_STORE_F32 ? f32x4{} : load_bias(bias_p, nb, q);
+            for (int q = 0; q < 4; ++q) bias[q] = epi_has_bias(EPI) ? load_bias(bias_p, nb, q) : f32x4{};
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int m = m0 + wm * C_::WTM + i * 32 + frow;
@@ -343,10 +412,25 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
                     const int n = nb + 8 * q;
                     if (!full && n >= g.N) continue;
                     f32x4 x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    if (EPI == EPI_STORE_F32) {
+                    if constexpr (EPI == EPI_STORE_F32) {
                         *reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n) = x;
+                    } else if constexpr (EPI == EPI_ACC_F32) {
+                        f32x4 *c = reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n);
+                        *c = *c + x;
+                    } else if constexpr (epi_act_grad(EPI)) {
+                        // gradient at the GeLU input: x * g'(u), u the saved GeLU input
+                        const bf16x4 u = *reinterpret_cast<const bf16x4 *>(aux_p + (int64_t)m * g.ldaux + n);
+                        const bf16x4 y = {(__bf16)(x[0] * act_grad<EPI>((float)u[0])),
+                                          (__bf16)(x[1] * act_grad<EPI>((float)u[1])),
+                                          (__bf16)(x[2] * act_grad<EPI>((float)u[2])),
+                                          (__bf16)(x[3] * act_grad<EPI>((float)u[3]))};
+                        *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * ldc + n) = y;
                     } else {
                         x += bias[q];
+                        if (aux_p) {   // keep the GeLU input for the backward pass
+                            const bf16x4 u = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+                            *reinterpret_cast<bf16x4 *>(aux_p + (int64_t)m * g.ldaux + n) = u;
+                        }
                         const bf16x4 y = {(__bf16)act<EPI>(x[0]), (__bf16)act<EPI>(x[1]), (__bf16)act<EPI>(x[2]),
                                           (__bf16)act<EPI>(x[3])};
                         *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * ldc + n) = y;
@@ -357,7 +441,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     }
 }
 
-template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI>
+template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s)
 {
     GemmDev g;
@@ -368,10 +452,12 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
         g.bias[b] = static_cast<const __bf16 *>(a.bias[src]);
         g.B2[b] = static_cast<const __bf16 *>(a.B2[src]);
         g.bias2[b] = static_cast<const __bf16 *>(a.bias2[src]);
+        g.aux[b] = static_cast<__bf16 *>(a.aux[src]);
         g.C[b] = a.C[src];
     }
     g.lda = a.lda;
     g.ldb = a.ldb;
+    g.ldaux = a.ldaux;
     for (int b = 0; b < kMaxBatch; ++b) g.ldc[b] = ldc_of(a, b < a.batch ? b : 0);
     g.M = (int)a.M;
     g.N = (int)a.N;
@@ -381,7 +467,7 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
     g.tiles_m = (int)((a.M + BM - 1) / BM);
     g.tiles_n = (int)((a.N + BNO - 1) / BNO);
     const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(NW * 64);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY>), grid, block, 0, s, g);
     return hipGetLastError();
 }
 
@@ -389,17 +475,34 @@ template <int BM, int BN, int BK, int S, int NW, bool IL>
 hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
 {
     constexpr bool gated_ok = Cfg<BM, BN, BK, S, NW>::TN % 2 == 0;
+    if (a.layout == LAYOUT_B_KMAJOR) {   // input gradients
+        switch (epi) {
+        case EPI_STORE_F32: return launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 1>(a, s);
+        case EPI_BIAS: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS, 1>(a, s);
+        case EPI_GELU_GRAD_TANH: return launch_one<BM, BN, BK, S, NW, IL, EPI_GELU_GRAD_TANH, 1>(a, s);
+        case EPI_GELU_GRAD_ERF: return launch_one<BM, BN, BK, S, NW, IL, EPI_GELU_GRAD_ERF, 1>(a, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (a.layout == LAYOUT_AB_KMAJOR) {  // weight gradients
+        switch (epi) {
+        case EPI_STORE_F32: return launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 2>(a, s);
+        case EPI_ACC_F32: return launch_one<BM, BN, BK, S, NW, IL, EPI_ACC_F32, 2>(a, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (epi) {
-    case EPI_BIAS_GELU: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU>(a, s);
-    case EPI_STORE_F32: return launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32>(a, s);
-    case EPI_BIAS_GELU_ERF: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU_ERF>(a, s);
-    case EPI_BIAS: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS>(a, s);
+    case EPI_BIAS_GELU: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU, 0>(a, s);
+    case EPI_STORE_F32: return launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 0>(a, s);
+    case EPI_BIAS_GELU_ERF: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU_ERF, 0>(a, s);
+    case EPI_BIAS: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS, 0>(a, s);
     case EPI_GATED_TANH:
-        if constexpr (gated_ok) return launch_one<BM, BN, BK, S, NW, IL, EPI_GATED_TANH>(a, s);
+        if constexpr (gated_ok) return launch_one<BM, BN, BK, S, NW, IL, EPI_GATED_TANH, 0>(a, s);
         break;
     case EPI_GATED_ERF:
-        if constexpr (gated_ok) return launch_one<BM, BN, BK, S, NW, IL, EPI_GATED_ERF>(a, s);
+        if constexpr (gated_ok) return launch_one<BM, BN, BK, S, NW, IL, EPI_GATED_ERF, 0>(a, s);
         break;
+    default: break;
     }
     return hipErrorInvalidValue;
 }

@@ -90,7 +90,59 @@ hipError_t launch_t(const PartialPtrs &P, const float *residual, float *out, voi
     return hipGetLastError();
 }
 
+// Column sums of a bf16 matrix X [M][N] (row stride ld) in fp32, in a fixed
+// order: a workgroup owns 32 columns; thread t reads 8 of them (16 bytes)
+// from rows t/4, t/4 + 64, t/4 + 128, ... with four loads in flight, and the
+// 64 row-lanes' sums are then added in row-lane order through LDS.
+__global__ void __launch_bounds__(256) colsum_kernel(const __bf16 *X, int64_t ld, int M, int N, float *out,
+                                                     int accumulate)
+{
+    __shared__ float part[64][33];
+    const int t = threadIdx.x, cc = t & 3, rl = t >> 2;
+    const int n0 = blockIdx.x * 32 + 8 * cc;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    auto add = [&](u32x4 w) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += __builtin_bit_cast(float, w[i] << 16);
+            acc[2 * i + 1] += __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+        }
+    };
+    if (n0 < N) {
+        const __bf16 *col = X + n0;
+        int m = rl;
+        for (; m + 3 * 64 < M; m += 4 * 64) {
+            u32x4 w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const u32x4 *>(col + (int64_t)(m + 64 * u) * ld);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) add(w[u]);
+        }
+        for (; m < M; m += 64) add(*reinterpret_cast<const u32x4 *>(col + (int64_t)m * ld));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rl][8 * cc + e] = acc[e];
+    __syncthreads();
+    if (t < 32) {
+        const int n = blockIdx.x * 32 + t;
+        float sum = 0.0f;
+        for (int r = 0; r < 64; ++r) sum += part[r][t];
+        if (n < N) out[n] = accumulate ? out[n] + sum : sum;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t M, int64_t N, float *out, bool accumulate,
+                              hipStream_t s)
+{
+    const unsigned grid = (unsigned)((N + 31) / 32);
+    hipLaunchKernelGGL(colsum_kernel, dim3(grid), dim3(256), 0, s, static_cast<const __bf16 *>(X), ld, (int)M, (int)N,
+                       out, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
 
 hipError_t launch_shard_reduce(const float *const *partials, int T, const float *residual, float *out,
                                void *out_bf16, int64_t M, int64_t H, bool rms, float eps, hipStream_t s)

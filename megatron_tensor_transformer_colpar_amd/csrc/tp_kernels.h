@@ -16,8 +16,20 @@ enum Epilogue : int {
     EPI_GATED_TANH = 3,     // GeLU_tanh(gate + bias[n]) * (up + bias2[n]), input dtype
     EPI_GATED_ERF = 4,      // GeLU_erf(gate + bias[n]) * (up + bias2[n]), input dtype
     EPI_BIAS = 5,           // + bias[n] (if any), no activation, input dtype
+    EPI_GELU_GRAD_TANH = 6, // acc * g'(aux[m][n]) (tanh-form GeLU derivative), bf16
+    EPI_GELU_GRAD_ERF = 7,  // acc * g'(aux[m][n]) (exact GeLU derivative), bf16
+    EPI_ACC_F32 = 8,        // C[m][n] += acc, fp32
 };
 constexpr bool epi_gated(int e) { return e == EPI_GATED_TANH || e == EPI_GATED_ERF; }
+constexpr bool epi_act_grad(int e) { return e == EPI_GELU_GRAD_TANH || e == EPI_GELU_GRAD_ERF; }
+constexpr bool epi_has_bias(int e) { return e == EPI_BIAS_GELU || e == EPI_BIAS_GELU_ERF || e == EPI_BIAS; }
+
+// Operand layouts of the bf16 MFMA GEMM (K-major: element (r, k) at k*ld + r).
+enum Layout : int {
+    LAYOUT_KCONTIG = 0,    // A [M][K], B [N][K]
+    LAYOUT_B_KMAJOR = 1,   // A [M][K], B stored [K][N]
+    LAYOUT_AB_KMAJOR = 2,  // A stored [K][M], B stored [K][N]
+};
 
 // C[m][n] = sum_k A[m][k] * B[n][k]  (both operands K-contiguous), then the
 // epilogue.  A: M rows, stride lda; B: N rows, stride ldb; C: stride ldc.
@@ -38,8 +50,11 @@ struct GemmArgs {
     void *C[kMaxBatch];
     int64_t ldc;
     int64_t ldc_b[kMaxBatch];      // per-problem row stride of C; 0 = ldc
+    void *aux[kMaxBatch];          // [M][N] bf16, stride ldaux: the GeLU input, written by the
+    int64_t ldaux;                 //   GeLU epilogues when set, read by the gradient epilogues
     int64_t M, N, K;
     int batch;
+    int layout;                    // Layout (bf16 MFMA GEMM only)
 };
 inline int64_t ldc_of(const GemmArgs &g, int b) { return g.ldc_b[b] ? g.ldc_b[b] : g.ldc; }
 
@@ -73,6 +88,11 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv);
 hipError_t launch_attn_bf16(const AttnArgs &a, int num_cu, hipStream_t s);
+
+// out[n] (+)= sum_m X[m][n] for a bf16 X [M][N] (row stride ld, N and ld
+// multiples of 8), fp32, in a fixed order.
+hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t M, int64_t N, float *out, bool accumulate,
+                              hipStream_t s);
 
 // out = (residual ? residual : 0) + sum_j partials[j]; optional bf16 copy,
 // optionally row-RMS-normalised.

@@ -60,9 +60,14 @@ raw.tp_attn_core.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i
                              _vp, ctypes.c_size_t, _vp]
 raw.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i32]
 raw.tp_attn_workspace_bytes.restype = ctypes.c_size_t
+raw.tp_colpar_act_train.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+raw.tp_rowpar_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _u32, _vp]
+raw.tp_colpar_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _u32, _vp]
+raw.tp_mlp_shard_bwd.argtypes = [_vp] * 11 + [_i64, _i64, _i64, _i32, _i32, _i32, _u32, _vp]
 for _f in (raw.tp_colpar_gelu, raw.tp_rowpar_partial, raw.tp_shard_reduce, raw.tp_mlp_shard_fwd,
            raw.tp_colpar_gelu_group, raw.tp_rowpar_partial_group, raw.tp_mlp_group_fwd, raw.tp_layer_fwd,
-           raw.tp_colpar_act, raw.tp_colpar_gated, raw.tp_colpar_linear, raw.tp_qkv_colpar, raw.tp_attn_core):
+           raw.tp_colpar_act, raw.tp_colpar_gated, raw.tp_colpar_linear, raw.tp_qkv_colpar, raw.tp_attn_core,
+           raw.tp_colpar_act_train, raw.tp_rowpar_bwd, raw.tp_colpar_bwd, raw.tp_mlp_shard_bwd):
     _f.restype = ctypes.c_int
 raw.tp_last_error.argtypes = []
 raw.tp_last_error.restype = ctypes.c_char_p
@@ -72,7 +77,9 @@ raw.tp_version.restype = ctypes.c_char_p
 EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_shard_fwd",
            "tp_colpar_gelu_group", "tp_rowpar_partial_group", "tp_mlp_group_fwd", "tp_layer_fwd",
            "tp_colpar_act", "tp_colpar_gated", "tp_colpar_linear", "tp_qkv_colpar", "tp_attn_core",
-           "tp_attn_workspace_bytes", "tp_last_error", "tp_version")
+           "tp_attn_workspace_bytes", "tp_colpar_act_train", "tp_rowpar_bwd", "tp_colpar_bwd", "tp_mlp_shard_bwd",
+           "tp_last_error", "tp_version")
+TP_GRAD_ACCUMULATE = 1
 TP_HEAD_DIM = 128
 
 
@@ -186,3 +193,25 @@ def tp_attn_core(Q, K, V, ctx, kv_len, Bs, Sq, Lk, nh, nkv, d, ldq, ldkv, ldo, c
 
 def tp_attn_workspace_bytes(Bs, Sq, Lk, nh, nkv) -> int:
     return int(raw.tp_attn_workspace_bytes(Bs, Sq, Lk, nh, nkv))
+
+
+def tp_colpar_act_train(X, W1t, b1, Y_i, U_i, M, H, F, T, i, act=TP_GELU_TANH, stream=None):
+    _check(raw.tp_colpar_act_train(_ptr(X), _ptr(W1t), _ptr(b1), _ptr(Y_i), _ptr(U_i), M, H, F, T, i, act,
+                                   _stream(stream)))
+
+
+def tp_rowpar_bwd(dZ, W2t, Y_i, U_i, dU_i, dW2t, M, H, F, T, i, act=TP_GELU_TANH, flags=0, stream=None):
+    _check(raw.tp_rowpar_bwd(_ptr(dZ), _ptr(W2t), _ptr(Y_i), _ptr(U_i), _ptr(dU_i), _ptr(dW2t), M, H, F, T, i, act,
+                             flags, _stream(stream)))
+
+
+def tp_colpar_bwd(X, W1t, dU_i, dX_i, dW1t, db1, M, H, F, T, i, flags=0, stream=None):
+    _check(raw.tp_colpar_bwd(_ptr(X), _ptr(W1t), _ptr(dU_i), _ptr(dX_i), _ptr(dW1t), _ptr(db1), M, H, F, T, i, flags,
+                             _stream(stream)))
+
+
+def tp_mlp_shard_bwd(X, W1t, W2t, U_i, Y_i, dZ, dU_ws, dX_i, dW1t, db1, dW2t, M, H, F, T, i, act=TP_GELU_TANH,
+                     flags=0, stream=None):
+    _check(raw.tp_mlp_shard_bwd(_ptr(X), _ptr(W1t), _ptr(W2t), _ptr(U_i), _ptr(Y_i), _ptr(dZ), _ptr(dU_ws),
+                                _ptr(dX_i), _ptr(dW1t), _ptr(db1), _ptr(dW2t), M, H, F, T, i, act, flags,
+                                _stream(stream)))
