@@ -433,6 +433,49 @@ def backward(args, torch, tp):
         log("[bench] backward %s: %s" % (label, e))
         del X, W1t, b1, W2t, dZ, Y, U, dU, dX, dW1t, db1, dW2t
         torch.cuda.empty_cache()
+    # the whole group of the 2048-token block (T=4): training forward and
+    # backward, one launch per projection over all ranks, then the backward
+    # all-reduce of the dX partials
+    M, H, F, T = 2048, 4096, 16384, 4
+    Fs = F // T
+    X, W1t, b1, W2t, dZ = (torch.randn(*sh, generator=g, device="cuda").mul(sd).to(torch.bfloat16)
+                           for sh, sd in (((M, H), 1.0), ((F, H), 0.02), ((F,), 0.01), ((H, F), 0.02), ((M, H), 1.0)))
+    Ys, Us, dUs = ([torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda") for _ in range(T)] for _ in range(3))
+    dXs = [torch.empty(M, H, dtype=torch.float32, device="cuda") for _ in range(T)]
+    dXsum = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    dW1t = torch.empty(F, H, dtype=torch.float32, device="cuda")
+    db1 = torch.empty(F, dtype=torch.float32, device="cuda")
+    dW2t = torch.empty(H, F, dtype=torch.float32, device="cuda")
+    ya, ua, da, xa = (tp.partial_array(v) for v in (Ys, Us, dUs, dXs))
+    fwd = lambda: tp.tp_mlp_group_fwd_train(X, W1t, b1, ya, ua, M, H, F, T, T1, stream)
+    bwd = lambda: tp.tp_mlp_group_bwd(X, W1t, W2t, ua, ya, dZ, da, xa, dW1t, db1, dW2t, M, H, F, T, T1, 0, stream)
+    red = lambda: tp.tp_shard_reduce(xa, T, None, dXsum, None, M, H, 0, stream)
+    ms = {}
+    n = max(3, args.steps // 5)
+    for name, f in (("forward_train", fwd), ("backward", bwd), ("dX_reduce", red)):
+        for _ in range(2):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / n
+    fl = 2.0 * M * H * F
+    grp = {"workload": "gpt_block_shard, all 4 ranks: M=2048 H=4096 F=16384 T=4"}
+    t = fl / (ms["forward_train"] * 1e-3) / 1e12
+    grp["forward_train"] = {"us": round(ms["forward_train"] * 1e3, 2), "tflops": round(t, 1),
+                            "frac": round(t / PEAK_BF16_TFLOPS, 4)}
+    t = 4 * fl / (ms["backward"] * 1e-3) / 1e12
+    grp["backward"] = {"us": round(ms["backward"] * 1e3, 2), "tflops": round(t, 1), "frac": round(t / PEAK_BF16_TFLOPS, 4)}
+    by = (T + 1) * M * H * 4
+    grp["dX_reduce"] = {"us": round(ms["dX_reduce"] * 1e3, 2), "gbs": round(by / (ms["dX_reduce"] * 1e-3) / 1e9, 1)}
+    out["group"] = grp
+    log("[bench] backward group: %s" % grp)
+    del X, W1t, b1, W2t, dZ, Ys, Us, dUs, dXs, dXsum, dW1t, db1, dW2t
+    torch.cuda.empty_cache()
     return out
 
 

@@ -399,6 +399,28 @@ tp_status tp_mlp_shard_bwd(const void *X, const void *W1t, const void *W2t, cons
                            int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, tp_act act, uint32_t flags,
                            hipStream_t stream);
 
+/*
+ * The whole TP group's training forward and backward on one GPU (the
+ * emulation of every rank, as tp_mlp_group_fwd; [LESSON] section 1), one
+ * launch per projection over the tiles of all T ranks:
+ *   tp_mlp_group_fwd_train: Y_ws[j] = g(U_ws[j]), U_ws[j] = X W1[:,C_j] + b1[C_j]
+ *   tp_mlp_group_bwd: for every rank j, dU_ws[j] = (dZ W2[C_j,:]^T) * g'(U_ws[j]),
+ *     dX_parts[j] = dU_ws[j] W1[:,C_j]^T (fp32 partials: tp_shard_reduce of
+ *     them is the backward all-reduce), and the whole dW1t [F][H], db1 [F],
+ *     dW2t [H][F] (fp32, written or accumulated: every rank's block).
+ * U_ws, Y_ws, dU_ws, dX_parts: HOST arrays of T device pointers.
+ * Validation: as tp_mlp_group_fwd and the per-rank backward entry points;
+ * every pointer non-NULL (TP_ERR_NULL); no output overlapping an input or
+ * another output (TP_ERR_ALIAS).
+ */
+tp_status tp_mlp_group_fwd_train(const void *X, const void *W1t, const void *b1, void *const *Y_ws,
+                                 void *const *U_ws, int64_t M, int64_t H, int64_t F, int32_t T, tp_act act,
+                                 hipStream_t stream);
+tp_status tp_mlp_group_bwd(const void *X, const void *W1t, const void *W2t, void *const *U_ws,
+                           void *const *Y_ws, const void *dZ, void *const *dU_ws, float *const *dX_parts,
+                           float *dW1t, float *db1, float *dW2t, int64_t M, int64_t H, int64_t F, int32_t T,
+                           tp_act act, uint32_t flags, hipStream_t stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *tp_last_error(void);
 

@@ -814,6 +814,154 @@ tp_status tp_mlp_shard_bwd(const void *X, const void *W1t, const void *W2t, cons
     return ok();
 }
 
+tp_status tp_mlp_group_fwd_train(const void *X, const void *W1t, const void *b1, void *const *Y_ws, void *const *U_ws,
+                                 int64_t M, int64_t H, int64_t F, int32_t T, tp_act act, hipStream_t stream)
+{
+    const char *fn = "tp_mlp_group_fwd_train";
+    tp_status st = validate_group(fn, X, W1t, b1, nullptr, Y_ws, nullptr, M, H, F, T, TP_BF16);
+    if (st != TP_OK) return st;
+    if ((st = check_act(fn, act)) != TP_OK) return st;
+    if (!U_ws) return fail(TP_ERR_NULL, "%s: U_ws must be non-NULL", fn);
+    const int64_t Fs = F / T;
+    for (int j = 0; j < T; ++j) {
+        if (!U_ws[j]) return fail(TP_ERR_NULL, "%s: shard %d's U buffer is NULL", fn, j);
+        if (!aligned16(U_ws[j])) return fail(TP_ERR_UNSUPPORTED, "%s: U buffers must be 16-byte aligned", fn);
+    }
+    if (M > 0) {
+        const Range in[3] = {span(X, M * H * 2), span(W1t, F * H * 2), span_or_none(b1, F * 2)};
+        for (int j = 0; j < T; ++j) {
+            const Range u = span(U_ws[j], M * Fs * 2);
+            for (const Range &r : in)
+                if (overlap(u, r)) return fail(TP_ERR_ALIAS, "%s: a U buffer overlaps an input", fn);
+            for (int k = 0; k < T; ++k)
+                if (overlap(u, span(Y_ws[k], M * Fs * 2)) || (k != j && overlap(u, span(U_ws[k], M * Fs * 2))))
+                    return fail(TP_ERR_ALIAS, "%s: a U buffer overlaps another shard buffer", fn);
+        }
+    }
+    if (M == 0) return ok();
+    tpk::GemmArgs g = colpar_args(X, W1t, b1, Y_ws, T, 0, M, H, F, T, TP_BF16);
+    for (int j = 0; j < T; ++j) g.aux[j] = U_ws[j];
+    g.ldaux = Fs;
+    const hipError_t e =
+        launch_mfma(g, act == TP_GELU_ERF ? tpk::EPI_BIAS_GELU_ERF : tpk::EPI_BIAS_GELU, tpk::LAYOUT_KCONTIG, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "group training column-parallel launch");
+}
+
+tp_status tp_mlp_group_bwd(const void *X, const void *W1t, const void *W2t, void *const *U_ws, void *const *Y_ws,
+                           const void *dZ, void *const *dU_ws, float *const *dX_parts, float *dW1t, float *db1,
+                           float *dW2t, int64_t M, int64_t H, int64_t F, int32_t T, tp_act act, uint32_t flags,
+                           hipStream_t stream)
+{
+    const char *fn = "tp_mlp_group_bwd";
+    tp_status st = check_bwd(fn, M, H, F, T, 0);
+    if (st != TP_OK) return st;
+    if (!X || !W1t || !W2t || !U_ws || !Y_ws || !dZ || !dU_ws || !dX_parts || !dW1t || !db1 || !dW2t)
+        return fail(TP_ERR_NULL, "%s: every pointer and pointer array must be non-NULL", fn);
+    for (int j = 0; j < T; ++j)
+        if (!U_ws[j] || !Y_ws[j] || !dU_ws[j] || !dX_parts[j])
+            return fail(TP_ERR_NULL, "%s: shard %d's buffer is NULL", fn, j);
+    if ((st = check_act(fn, act)) != TP_OK) return st;
+    if (flags & ~TP_GRAD_ACCUMULATE) return fail(TP_ERR_UNSUPPORTED, "%s: unknown flags 0x%x", fn, flags);
+    bool al = aligned16(X) && aligned16(W1t) && aligned16(W2t) && aligned16(dZ) && aligned16(dW1t) &&
+              aligned16(db1) && aligned16(dW2t);
+    for (int j = 0; j < T; ++j)
+        al = al && aligned16(U_ws[j]) && aligned16(Y_ws[j]) && aligned16(dU_ws[j]) && aligned16(dX_parts[j]);
+    if (!al) return fail(TP_ERR_UNSUPPORTED, "%s: every buffer must be 16-byte aligned", fn);
+    const int64_t Fs = F / T;
+    if (M > 0) {
+        Range out[3 + 2 * TP_MAX_T], in[4 + 2 * TP_MAX_T];
+        int no = 0, ni = 0;
+        out[no++] = span(dW1t, F * H * 4);
+        out[no++] = span(db1, F * 4);
+        out[no++] = span(dW2t, H * F * 4);
+        in[ni++] = span(X, M * H * 2);
+        in[ni++] = span(W1t, F * H * 2);
+        in[ni++] = span(W2t, H * F * 2);
+        in[ni++] = span(dZ, M * H * 2);
+        for (int j = 0; j < T; ++j) {
+            out[no++] = span(dU_ws[j], M * Fs * 2);
+            out[no++] = span(dX_parts[j], M * H * 4);
+            in[ni++] = span(U_ws[j], M * Fs * 2);
+            in[ni++] = span(Y_ws[j], M * Fs * 2);
+        }
+        if ((st = check_disjoint(fn, out, no, in, ni)) != TP_OK) return st;
+    }
+    if (M == 0) return ok();
+    const bool acc = flags & TP_GRAD_ACCUMULATE;
+    const tpk::Epilogue wepi = acc ? tpk::EPI_ACC_F32 : tpk::EPI_STORE_F32;
+    // every rank's dU_j = (dZ . W2[C_j,:]^T) * g'(U_j), one launch
+    tpk::GemmArgs g = empty_args();
+    g.batch = T;
+    for (int j = 0; j < T; ++j) {
+        g.A[j] = dZ;
+        g.B[j] = static_cast<const char *>(W2t) + (int64_t)j * Fs * 2;
+        g.C[j] = dU_ws[j];
+        g.aux[j] = U_ws[j];
+    }
+    g.lda = H;
+    g.ldb = F;
+    g.ldc = Fs;
+    g.ldaux = Fs;
+    g.M = M;
+    g.N = Fs;
+    g.K = H;
+    hipError_t e = launch_mfma(g, act == TP_GELU_ERF ? tpk::EPI_GELU_GRAD_ERF : tpk::EPI_GELU_GRAD_TANH,
+                               tpk::LAYOUT_B_KMAJOR, stream);
+    if (e != hipSuccess) return hip_fail(e, "group input-gradient launch");
+    // dW2[C_j,:]: columns C_j of dW2^T, one launch
+    tpk::GemmArgs w2 = empty_args();
+    w2.batch = T;
+    for (int j = 0; j < T; ++j) {
+        w2.A[j] = dZ;
+        w2.B[j] = Y_ws[j];
+        w2.C[j] = dW2t + (int64_t)j * Fs;
+    }
+    w2.lda = H;
+    w2.ldb = Fs;
+    w2.ldc = F;
+    w2.M = H;
+    w2.N = Fs;
+    w2.K = M;
+    if ((e = launch_mfma(w2, wepi, tpk::LAYOUT_AB_KMAJOR, stream)) != hipSuccess)
+        return hip_fail(e, "group weight-gradient launch");
+    // dX_j = dU_j . W1[:,C_j]^T, the partials of the backward all-reduce, one launch
+    tpk::GemmArgs x = empty_args();
+    x.batch = T;
+    for (int j = 0; j < T; ++j) {
+        x.A[j] = dU_ws[j];
+        x.B[j] = static_cast<const char *>(W1t) + (int64_t)j * Fs * H * 2;
+        x.C[j] = dX_parts[j];
+    }
+    x.lda = Fs;
+    x.ldb = H;
+    x.ldc = H;
+    x.M = M;
+    x.N = H;
+    x.K = Fs;
+    if ((e = launch_mfma(x, tpk::EPI_STORE_F32, tpk::LAYOUT_B_KMAJOR, stream)) != hipSuccess)
+        return hip_fail(e, "group input-gradient partial launch");
+    // dW1[:,C_j]: rows C_j of dW1^T, one launch
+    tpk::GemmArgs w1 = empty_args();
+    w1.batch = T;
+    for (int j = 0; j < T; ++j) {
+        w1.A[j] = dU_ws[j];
+        w1.B[j] = X;
+        w1.C[j] = dW1t + (int64_t)j * Fs * H;
+    }
+    w1.lda = Fs;
+    w1.ldb = H;
+    w1.ldc = H;
+    w1.M = Fs;
+    w1.N = H;
+    w1.K = M;
+    if ((e = launch_mfma(w1, wepi, tpk::LAYOUT_AB_KMAJOR, stream)) != hipSuccess)
+        return hip_fail(e, "group weight-gradient launch");
+    for (int j = 0; j < T; ++j)
+        if ((e = tpk::launch_colsum_bf16(dU_ws[j], Fs, M, Fs, db1 + (int64_t)j * Fs, acc, stream)) != hipSuccess)
+            return hip_fail(e, "group bias-gradient launch");
+    return ok();
+}
+
 const char *tp_last_error(void) { return g_err.c_str(); }
 
 const char *tp_version(void) { return "tp_colpar 0.1.0 gfx950"; }

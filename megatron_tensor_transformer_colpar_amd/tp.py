@@ -64,10 +64,14 @@ raw.tp_colpar_act_train.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _
 raw.tp_rowpar_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _u32, _vp]
 raw.tp_colpar_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _u32, _vp]
 raw.tp_mlp_shard_bwd.argtypes = [_vp] * 11 + [_i64, _i64, _i64, _i32, _i32, _i32, _u32, _vp]
+raw.tp_mlp_group_fwd_train.argtypes = [_vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
+raw.tp_mlp_group_bwd.argtypes = [_vp, _vp, _vp, _pp, _pp, _vp, _pp, _pp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+                                 _u32, _vp]
 for _f in (raw.tp_colpar_gelu, raw.tp_rowpar_partial, raw.tp_shard_reduce, raw.tp_mlp_shard_fwd,
            raw.tp_colpar_gelu_group, raw.tp_rowpar_partial_group, raw.tp_mlp_group_fwd, raw.tp_layer_fwd,
            raw.tp_colpar_act, raw.tp_colpar_gated, raw.tp_colpar_linear, raw.tp_qkv_colpar, raw.tp_attn_core,
-           raw.tp_colpar_act_train, raw.tp_rowpar_bwd, raw.tp_colpar_bwd, raw.tp_mlp_shard_bwd):
+           raw.tp_colpar_act_train, raw.tp_rowpar_bwd, raw.tp_colpar_bwd, raw.tp_mlp_shard_bwd,
+           raw.tp_mlp_group_fwd_train, raw.tp_mlp_group_bwd):
     _f.restype = ctypes.c_int
 raw.tp_last_error.argtypes = []
 raw.tp_last_error.restype = ctypes.c_char_p
@@ -78,7 +82,7 @@ EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_sha
            "tp_colpar_gelu_group", "tp_rowpar_partial_group", "tp_mlp_group_fwd", "tp_layer_fwd",
            "tp_colpar_act", "tp_colpar_gated", "tp_colpar_linear", "tp_qkv_colpar", "tp_attn_core",
            "tp_attn_workspace_bytes", "tp_colpar_act_train", "tp_rowpar_bwd", "tp_colpar_bwd", "tp_mlp_shard_bwd",
-           "tp_last_error", "tp_version")
+           "tp_mlp_group_fwd_train", "tp_mlp_group_bwd", "tp_last_error", "tp_version")
 TP_GRAD_ACCUMULATE = 1
 TP_HEAD_DIM = 128
 
@@ -214,4 +218,16 @@ def tp_mlp_shard_bwd(X, W1t, W2t, U_i, Y_i, dZ, dU_ws, dX_i, dW1t, db1, dW2t, M,
                      flags=0, stream=None):
     _check(raw.tp_mlp_shard_bwd(_ptr(X), _ptr(W1t), _ptr(W2t), _ptr(U_i), _ptr(Y_i), _ptr(dZ), _ptr(dU_ws),
                                 _ptr(dX_i), _ptr(dW1t), _ptr(db1), _ptr(dW2t), M, H, F, T, i, act, flags,
+                                _stream(stream)))
+
+
+def tp_mlp_group_fwd_train(X, W1t, b1, Y_ws, U_ws, M, H, F, T, act=TP_GELU_TANH, stream=None):
+    _check(raw.tp_mlp_group_fwd_train(_ptr(X), _ptr(W1t), _ptr(b1), _arr(Y_ws), _arr(U_ws), M, H, F, T, act,
+                                      _stream(stream)))
+
+
+def tp_mlp_group_bwd(X, W1t, W2t, U_ws, Y_ws, dZ, dU_ws, dX_parts, dW1t, db1, dW2t, M, H, F, T, act=TP_GELU_TANH,
+                     flags=0, stream=None):
+    _check(raw.tp_mlp_group_bwd(_ptr(X), _ptr(W1t), _ptr(W2t), _arr(U_ws), _arr(Y_ws), _ptr(dZ), _arr(dU_ws),
+                                _arr(dX_parts), _ptr(dW1t), _ptr(db1), _ptr(dW2t), M, H, F, T, act, flags,
                                 _stream(stream)))

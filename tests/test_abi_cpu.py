@@ -366,3 +366,79 @@ def test_attention_empty_calls_are_ok():
     assert attn(Bs=0) == tp.TP_OK
     assert attn(Sq=0, causal=0) == tp.TP_OK
     assert tp.last_error() == ""
+
+
+# ------------------------------------------------------------ backward pass
+def rowpar_bwd(dZ=P[0], W2t=P[1], Y=P[2], U=P[3], dU=P[4], dW2t=P[5], M=4, H=64, F=256, T=4, i=0,
+               act=tp.TP_GELU_TANH, flags=0):
+    return tp.raw.tp_rowpar_bwd(dZ, W2t, Y, U, dU, dW2t, M, H, F, T, i, act, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), tp.TP_ERR_SHAPE),
+    (dict(i=4), tp.TP_ERR_SHAPE),
+    (dict(dZ=None), tp.TP_ERR_NULL),
+    (dict(dU=None), tp.TP_ERR_NULL),
+    (dict(Y=None), tp.TP_ERR_NULL),          # the weight gradient needs Y_i
+    (dict(act=9), tp.TP_ERR_UNSUPPORTED),
+    (dict(flags=2), tp.TP_ERR_UNSUPPORTED),
+    (dict(H=96), tp.TP_ERR_UNSUPPORTED),
+    (dict(M=1 << 20, H=4096, F=4096, T=1), tp.TP_ERR_UNSUPPORTED),   # 32-bit offsets
+    (dict(dW2t=P[5] + 4), tp.TP_ERR_UNSUPPORTED),
+    (dict(dU=P[2]), tp.TP_ERR_ALIAS),        # dU over Y_i
+    (dict(dW2t=P[1]), tp.TP_ERR_ALIAS),      # dW2 over W2
+])
+def test_rowpar_bwd_rejects(kw, status):
+    assert rowpar_bwd(**kw) == status
+    assert "tp_rowpar_bwd" in tp.last_error()
+
+
+def colpar_bwd(X=P[0], W1t=P[1], dU=P[2], dX=P[3], dW1t=P[4], db1=P[5], M=4, H=64, F=256, T=4, i=1, flags=0):
+    return tp.raw.tp_colpar_bwd(X, W1t, dU, dX, dW1t, db1, M, H, F, T, i, flags, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=3), tp.TP_ERR_SHAPE),
+    (dict(dU=None), tp.TP_ERR_NULL),
+    (dict(W1t=None), tp.TP_ERR_NULL),        # dX needs W1t
+    (dict(X=None), tp.TP_ERR_NULL),          # dW1 needs X
+    (dict(flags=8), tp.TP_ERR_UNSUPPORTED),
+    (dict(db1=P[5] + 8), tp.TP_ERR_UNSUPPORTED),
+    (dict(dX=P[2]), tp.TP_ERR_ALIAS),        # dX over dU
+    (dict(db1=P[4] + 64), tp.TP_ERR_ALIAS),  # db1 inside dW1
+])
+def test_colpar_bwd_rejects(kw, status):
+    assert colpar_bwd(**kw) == status
+    assert "tp_colpar_bwd" in tp.last_error()
+
+
+def test_backward_optional_outputs_and_empty_calls():
+    assert colpar_bwd(M=0) == tp.TP_OK
+    assert rowpar_bwd(M=0) == tp.TP_OK
+    # without the outputs that need them, X / W1t / Y_i may be NULL (M = 0: nothing launched)
+    assert colpar_bwd(X=None, W1t=None, dX=None, dW1t=None, M=0) == tp.TP_OK
+    assert rowpar_bwd(Y=None, dW2t=None, U=None, M=0) == tp.TP_OK
+    assert tp.raw.tp_colpar_act_train(P[0], P[1], P[2], P[3], P[4], 0, 64, 256, 4, 0, 0, None) == tp.TP_OK
+    assert tp.last_error() == ""
+
+
+def test_training_forward_rejects():
+    f = tp.raw.tp_colpar_act_train
+    assert f(P[0], P[1], P[2], P[3], None, 4, 64, 256, 4, 0, 0, None) == tp.TP_ERR_NULL
+    assert f(P[0], P[1], P[2], P[3], P[3] + 16, 4, 64, 256, 4, 0, 0, None) == tp.TP_ERR_ALIAS
+    assert f(P[0], P[1], P[2], P[3], P[4], 4, 64, 256, 4, 0, 5, None) == tp.TP_ERR_UNSUPPORTED
+    assert "tp_colpar_act_train" in tp.last_error()
+
+
+def test_shard_and_group_backward_reject():
+    assert tp.raw.tp_mlp_shard_bwd(P[0], P[1], P[2], None, P[4], P[5], P[6], P[7], P[8], P[9], P[10], 4, 64, 256,
+                                   4, 0, 0, 0, None) == tp.TP_ERR_NULL
+    arr = lambda *xs: tp.partial_array(list(xs))
+    U, Y, dU, dX = arr(P[3], P[3] + 4096), arr(P[4], P[4] + 4096), arr(P[6], P[6] + 4096), arr(P[7], P[7] + 8192)
+    g = tp.raw.tp_mlp_group_bwd
+    assert g(P[0], P[1], P[2], U, Y, P[5], dU, dX, P[8], P[9], P[10], 4, 64, 256, 3, 0, 0, None) == tp.TP_ERR_SHAPE
+    assert g(P[0], P[1], None, U, Y, P[5], dU, dX, P[8], P[9], P[10], 4, 64, 256, 2, 0, 0, None) == tp.TP_ERR_NULL
+    bad = arr(P[7], P[7])     # two ranks' dX partials on one buffer
+    assert g(P[0], P[1], P[2], U, Y, P[5], dU, bad, P[8], P[9], P[10], 4, 64, 256, 2, 0, 0, None) == tp.TP_ERR_ALIAS
+    assert g(P[0], P[1], P[2], U, Y, P[5], dU, dX, P[8], P[9], P[10], 0, 64, 256, 2, 0, 0, None) == tp.TP_OK
+    assert "" == tp.last_error()

@@ -228,3 +228,45 @@ def test_backward_full_size_sampled():
     er = rel_fro(to_f64(dX)[rows], orow["dX_i"])
     print("  rows: dX %.2e" % er)
     assert er <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T,M", [(4, 256), (2, 130)])
+def test_group_entry_points(T, M):
+    # the whole group's training forward and backward, one launch per
+    # projection: against the unsharded oracle gradients and the per-rank calls
+    H, F = 512, 2048
+    p = Problem(76, M, H, F, T, TANH)
+    Fs = F // T
+    bf = lambda: torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+    Ys, Us, dUs = [bf() for _ in range(T)], [bf() for _ in range(T)], [bf() for _ in range(T)]
+    dXs = [torch.empty(M, H, dtype=torch.float32, device="cuda") for _ in range(T)]
+    dW1t = torch.empty(F, H, dtype=torch.float32, device="cuda")
+    db1 = torch.empty(F, dtype=torch.float32, device="cuda")
+    dW2t = torch.empty(H, F, dtype=torch.float32, device="cuda")
+    tp.tp_mlp_group_fwd_train(p.dX_, p.dW1t, p.db1, Ys, Us, M, H, F, T)
+    tp.tp_mlp_group_bwd(p.dX_, p.dW1t, p.dW2t, Us, Ys, p.ddZ, dUs, dXs, dW1t, db1, dW2t, M, H, F, T)
+    dX = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    tp.tp_shard_reduce(dXs, T, None, dX, None, M, H)
+    torch.cuda.synchronize()
+    o = p.oracle(T=1, i=0)
+    e = (rel_fro(to_f64(dX), o["dX_i"]), rel_fro(to_f64(dW1t).T, o["dW1_i"]), rel_fro(to_f64(db1), o["db1_i"]),
+         rel_fro(to_f64(dW2t).T, o["dW2_i"]))
+    print("  dX %.2e dW1 %.2e db1 %.2e dW2 %.2e" % e)
+    assert max(e) <= TOL["bf16"]
+    # the per-rank entry points give the same numbers
+    for i in (0, T - 1):
+        Y, U = p.forward_train(i)
+        dU = torch.empty_like(Y)
+        dXi = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        w1 = torch.empty(F, H, dtype=torch.float32, device="cuda")
+        b = torch.empty(F, dtype=torch.float32, device="cuda")
+        w2 = torch.empty(H, F, dtype=torch.float32, device="cuda")
+        tp.tp_mlp_shard_bwd(p.dX_, p.dW1t, p.dW2t, U, Y, p.ddZ, dU, dXi, w1, b, w2, M, H, F, T, i)
+        torch.cuda.synchronize()
+        sl = slice(i * Fs, (i + 1) * Fs)
+        assert torch.equal(Y, Ys[i]) and torch.equal(U, Us[i])
+        d = max(rel_fro(to_f64(dU), to_f64(dUs[i])), rel_fro(to_f64(dXi), to_f64(dXs[i])),
+                rel_fro(to_f64(w1[sl]), to_f64(dW1t[sl])), rel_fro(to_f64(w2[:, sl]), to_f64(dW2t[:, sl])),
+                rel_fro(to_f64(b[sl]), to_f64(db1[sl])))
+        print("  rank %d: group vs per-rank %.1e" % (i, d))
+        assert d <= 1e-6
