@@ -324,6 +324,8 @@ hipError_t launch_gemv_bf16(const GemmArgs &a, Epilogue epi, int num_cu, hipStre
         return two ? launch_mt<EPI_GATED_ERF, 2>(g, a.batch, num_cu, s) : launch_mt<EPI_GATED_ERF, 1>(g, a.batch, num_cu, s);
     case EPI_BIAS:
         return two ? launch_mt<EPI_BIAS, 2>(g, a.batch, num_cu, s) : launch_mt<EPI_BIAS, 1>(g, a.batch, num_cu, s);
+    default:   // the gradient epilogues run on the MFMA GEMM only
+        break;
     }
     return hipErrorInvalidValue;
 }

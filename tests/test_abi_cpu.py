@@ -442,3 +442,10 @@ def test_shard_and_group_backward_reject():
     assert g(P[0], P[1], P[2], U, Y, P[5], dU, bad, P[8], P[9], P[10], 4, 64, 256, 2, 0, 0, None) == tp.TP_ERR_ALIAS
     assert g(P[0], P[1], P[2], U, Y, P[5], dU, dX, P[8], P[9], P[10], 0, 64, 256, 2, 0, 0, None) == tp.TP_OK
     assert "" == tp.last_error()
+
+
+def test_build_compiles_every_kernel_source():
+    # every HIP source next to the ABI is part of the library build
+    from megatron_tensor_transformer_colpar_amd import build
+    hip = sorted(f for f in os.listdir(build.CSRC) if f.endswith(".hip"))
+    assert hip and set(hip) <= set(build.SOURCES)
