@@ -170,35 +170,54 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt, in
     const int vbyte = (4 * h + rr) * 256 + 16 * vlow + 8 * (lane & 1);
 
     if (ntiles > 0) issue(k0_lds, v0_lds, 0);
-    if (ntiles > 1) issue(k1_lds, v1_lds, 1);
 
     float m_run = -1e30f, l_run = 0.0f;
     f32x16 acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
     const int my_pos = off + q0 + col;
+    // loop-invariant lane offsets: the V transpose reads of each d-block,
+    // and the partner lane (the other key half of the same query)
+    int vt_off[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) vt_off[db] = vbyte + 64 * (db ^ rr);
+    const int half_swap = (lane ^ 32) << 2;
 
-    // one key tile from the stage (kst, vst), which is then refilled with tile kt + 2
-    auto tile = [&](int kt, u32x4 *kst, u32x4 *vst) __attribute__((always_inline)) {
-        if (kt + 1 < ntiles)
-            __builtin_amdgcn_s_waitcnt(wait_vm(8));
-        else
-            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    // One key tile from the stage (kst, vst).  A single barrier per tile:
+    // once every wave has passed it, tile kt has landed and no wave still
+    // reads the other stage (tile kt-1), which is then refilled with tile
+    // kt+1 while this tile is computed.
+    auto tile = [&](int kt, u32x4 *kst, u32x4 *vst, u32x4 *kother, u32x4 *vother) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(wait_vm(0) & kWaitLgkm0);
         __builtin_amdgcn_s_barrier();
+        if (kt + 1 < ntiles) issue(kother, vother, kt + 1);
 
         const int k0 = kt * kBK;
         if (w_rows && (!a.causal || k0 <= w_last_pos)) {
             // S^T tile: keys (k0 + 32kb + ...) x this wave's 32 queries
             f32x16 s[2] = {f32x16{}, f32x16{}};
+            bf16x8 kf[8][2];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < 8; ++t)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int row = kb * 32 + col;
-                    const bf16x8 kf = __builtin_bit_cast(bf16x8, kst[kfrag + kb * 512 + ((2 * t + h) ^ (row & 15))]);
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[kb], 0, 0, 0);
-                }
+                for (int kb = 0; kb < 2; ++kb)   // row kb*32 + col, whose low 4 bits are col's
+                    kf[t][kb] = __builtin_bit_cast(bf16x8, kst[kfrag + kb * 512 + ((2 * t + h) ^ (col & 15))]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][kb], qf[t], s[kb], 0, 0, 0);
+            // the fragment reads run two k-steps ahead of the MFMAs (left
+            // alone, the scheduler issues each pair of reads right before
+            // its MFMAs and waits out the LDS latency every time)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int t = 0; t < 6; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_barrier(0);
             // lane: query q0 + col; element r of s[kb]: key k0 + 32kb + 8(r/4) + 4h + r%4.
             // Only tiles on the diagonal or past the sequence's end need the mask.
             if ((k0 + kBK > len) || (a.causal && k0 + kBK - 1 > off + q0)) {
@@ -216,7 +235,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt, in
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+            mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(half_swap, __builtin_bit_cast(int, mx)))) *
+                 a.scale_log2;
             // Lazy rescale: the reference max m_run (log2 units) only moves
             // when a tile's max exceeds it by more than 8, so the weights stay
             // <= 2^8 and the output is rescaled only on those tiles; the sum
@@ -250,7 +270,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt, in
                     const int kbase = (kb * 32 + ks * 16) * 256;
 #pragma unroll
                     for (int db = 0; db < 4; ++db) {
-                        const int o = kbase + vbyte + 64 * (db ^ rr);
+                        const int o = kbase + vt_off[db];
                         const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(vt + o));
                         const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(vt + o + 8 * 256));
                         const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -258,14 +278,10 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnDev a, int nqt, in
                     }
                 }
         }
-        // every wave is done with this stage before it is refilled
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();
-        if (kt + 2 < ntiles) issue(kst, vst, kt + 2);
     };
     for (int kt = 0; kt < ntiles; kt += 2) {
-        tile(kt, k0_lds, v0_lds);
-        if (kt + 1 < ntiles) tile(kt + 1, k1_lds, v1_lds);
+        tile(kt, k0_lds, v0_lds, k1_lds, v1_lds);
+        if (kt + 1 < ntiles) tile(kt + 1, k1_lds, v1_lds, k0_lds, v0_lds);
     }
 
     // normalise and store: lane holds query q0 + col, dims 32db + 8(r/4) + 4h + r%4
