@@ -1,0 +1,48 @@
+"""Host logic of bench.py, on the CPU: the one-GPU guard exits before any GPU
+work, and the committed HBM traffic record is used only while the kernel
+source it was measured on is unchanged."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("argv, env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "4"})])
+def test_more_than_one_gpu_is_refused(argv, env):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + argv, capture_output=True, text=True,
+                       env=dict(os.environ, **env), timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_record_matches_the_current_source():
+    # the committed counters were taken on the GEMM source as it stands
+    recs = json.load(open(bench.TRAFFIC_FILE))
+    for key in ("gemm_up_gelu@gpt_block_shard", "gemm_rowpar_partial@gpt_block_shard"):
+        rec = recs[key]
+        assert rec["source_sha"] == bench.source_sha(rec["source"]), key
+        t = bench.measured_traffic(key)
+        assert t is not None and t["total_bytes"] == rec["fetch_bytes"] + rec["write_bytes"]
+        assert t["total_bytes"] > rec["algorithmic_bytes"] > 0
+
+
+def test_stale_or_missing_traffic_record_reads_as_none(tmp_path, monkeypatch):
+    recs = json.load(open(bench.TRAFFIC_FILE))
+    key = "gemm_rowpar_partial@gpt_block_shard"
+    stale = dict(recs)
+    stale[key] = dict(recs[key], source_sha="0" * 16)
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps(stale))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
+    assert bench.measured_traffic(key) is None
+    assert bench.measured_traffic("no_such_kernel") is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
+    assert bench.measured_traffic(key) is None
