@@ -645,6 +645,18 @@ def stack80(args, torch, tp):
     return out
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, or None where it is not readable."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(args, hl):
     import numpy as np
 
@@ -675,7 +687,8 @@ def cpu_baseline(args, hl):
     log("[bench] cpu oracle: %d rows in %.2fs (%.3f GFLOP/s), parity %.2e" % (len(rows), dt, tflops * 1e3, err))
     cb = {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
           "sample": "%d of %d token rows of the headline step (all %d shards + reduce, fp64), %.1f s"
-                    % (len(rows), w.M, w.T, dt)}
+                    % (len(rows), w.M, w.T, dt),
+          "cpu_model": cpu_model()}
     par = {"rows": len(rows), "rel_fro_Z": err, "tol": 5e-3, "ok": err <= 5e-3}
     return cb, par
 

@@ -46,3 +46,8 @@ def test_stale_or_missing_traffic_record_reads_as_none(tmp_path, monkeypatch):
     assert bench.measured_traffic("no_such_kernel") is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
     assert bench.measured_traffic(key) is None
+
+
+def test_cpu_model_is_a_string_or_none():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
