@@ -165,7 +165,13 @@ __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
 // on the read (k-step s, lane (g, r)), conflict-free both ways.  A lane's
 // fragment holds the same k values as in gemv_bf16_kernel, so for the same
 // split of K the sums are formed in the same order.  D units (loads of
-// weights and tokens) are kept in flight per wave.
+// weights and tokens) are kept in flight per wave.  With two token tiles
+// (M > 16) the token rows are read the same way (a 16-token x 128-k unit is
+// a weight unit's shape) and regrouped through the same slot after the
+// weights: read straight into fragments, each token load touched 16
+// half-used cache lines instead of 8 whole ones, and those line accesses
+// bound the kernel at M = 32 (measured 17% faster; the 16-wave kernel keeps
+// direct token loads, where the regroup's registers would spill).
 template <int EPI, int MT, int KS, int D>
 __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
 {
@@ -197,9 +203,16 @@ __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
         wslot[i] = i * 64 + a * 16 + (b ^ (4 * i + a));
         rslot[i] = (b >> 2) * 64 + (b & 3) * 16 + ((4 * i + a) ^ b);
     }
+    // token rows: regrouped (instruction i reads tokens 16mt + 4i + a, 256
+    // contiguous bytes each) or read straight into fragments (lane: token
+    // 16mt + b, k-chunk a of the 32-wide k-step i)
+    constexpr bool XR = MT == 2 && KS <= 8;
     uint32_t x_voff[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) x_voff[mt] = (uint32_t)(((mt * 16 + b) * g.ldx + kbeg + 8 * a) * 2);
+    for (int mt = 0; mt < MT; ++mt)
+        x_voff[mt] = XR ? (uint32_t)(((mt * 16 + a) * g.ldx + kbeg) * 2 + b * 16)
+                        : (uint32_t)(((mt * 16 + b) * g.ldx + kbeg + 8 * a) * 2);
+    const uint32_t x_istep = XR ? (uint32_t)(4 * g.ldx * 2) : 64u;
 
     f32x4 acc[MT];
 #pragma unroll
@@ -218,7 +231,7 @@ __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) xv[d][s][mt] = buf_load16(xsrc, x_voff[mt] + s * 64, (uint32_t)so);
+            for (int mt = 0; mt < MT; ++mt) xv[d][s][mt] = buf_load16(xsrc, x_voff[mt] + s * x_istep, (uint32_t)so);
     };
     auto step = [&](int u, int d) __attribute__((always_inline)) {
 #pragma unroll
@@ -226,6 +239,16 @@ __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
         u32x4 f[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) f[s] = ulds[w][rslot[s]];
+        if constexpr (XR) {
+            // the slot is reused: a wave's LDS operations complete in order
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ulds[w][wslot[i]] = xv[d][i][mt];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) xv[d][s][mt] = ulds[w][rslot[s]];
+            }
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
