@@ -170,8 +170,8 @@ __global__ void __launch_bounds__(KS * 64) gemv_bf16_kernel(GemvDev g)
 // a weight unit's shape) and regrouped through the same slot after the
 // weights: read straight into fragments, each token load touched 16
 // half-used cache lines instead of 8 whole ones, and those line accesses
-// bound the kernel at M = 32 (measured 17% faster; the 16-wave kernel keeps
-// direct token loads, where the regroup's registers would spill).
+// bound the kernel at M = 32 (measured 17% faster).  Sixteen-wave blocks
+// have no registers for the regroup and run with one token tile only.
 template <int EPI, int MT, int KS, int D>
 __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
 {
@@ -206,7 +206,8 @@ __global__ void __launch_bounds__(KS * 64) gemv_seg_kernel(GemvDev g)
     // token rows: regrouped (instruction i reads tokens 16mt + 4i + a, 256
     // contiguous bytes each) or read straight into fragments (lane: token
     // 16mt + b, k-chunk a of the 32-wide k-step i)
-    constexpr bool XR = MT == 2 && KS <= 8;
+    constexpr bool XR = MT == 2;
+    static_assert(!(XR && KS > 8), "two token tiles run on at most eight waves");
     uint32_t x_voff[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -302,11 +303,16 @@ hipError_t launch_mt(const GemvDev &g, int batch, int num_cu, hipStream_t s)
     // with fewer blocks than CUs (a narrow projection such as one rank's
     // query, key or value block) has too few bytes in flight at eight
     // waves: it takes sixteen, each wave with two 4 KiB units in flight.
-    const int blocks = g.N / (epi_gated(EPI) ? 8 : 16) * batch;
-    if (blocks < num_cu && (g.K / 16) % 128 == 0 && g.K / 16 >= 256) {
-        const dim3 grid((unsigned)(g.N / (epi_gated(EPI) ? 8 : 16)), (unsigned)batch);
-        hipLaunchKernelGGL((gemv_seg_kernel<EPI, MT, 16, 2>), grid, dim3(16 * 64), 0, s, g);
-        return hipGetLastError();
+    // With two token tiles it stays at eight waves, where the token rows are
+    // regrouped (sixteen waves have no registers for that); measured on one
+    // rank's decode Q/K/V projection at M = 32: 16.4 against 22.3 us.
+    if constexpr (MT == 1) {
+        const int blocks = g.N / (epi_gated(EPI) ? 8 : 16) * batch;
+        if (blocks < num_cu && (g.K / 16) % 128 == 0 && g.K / 16 >= 256) {
+            const dim3 grid((unsigned)(g.N / (epi_gated(EPI) ? 8 : 16)), (unsigned)batch);
+            hipLaunchKernelGGL((gemv_seg_kernel<EPI, MT, 16, 2>), grid, dim3(16 * 64), 0, s, g);
+            return hipGetLastError();
+        }
     }
     if (g.K % (8 * 64) == 0 && g.K / 8 >= 256) return launch_ks<EPI, MT, 8>(g, batch, s);
     if (g.K % (4 * 64) == 0 && g.K / 4 >= 256) return launch_ks<EPI, MT, 4>(g, batch, s);

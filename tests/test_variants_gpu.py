@@ -166,11 +166,13 @@ def test_gated_mlp_shards_reduce_to_the_unsharded_block():
 
 
 # --------------------------------------- narrow grids (fewer blocks than CUs)
+@pytest.mark.parametrize("M", [8, 32])
 @pytest.mark.parametrize("kind", ["gelu", "gated", "rowpar"])
-def test_narrow_skinny_grid_sixteen_waves(kind):
-    # K = 4096 and so few output columns that the skinny-M stream runs
-    # sixteen waves per block: every epilogue on that configuration
-    M, H = 8, 4096
+def test_narrow_skinny_grid(kind, M):
+    # K = 4096 and fewer blocks than CUs: with one token tile (M = 8) the
+    # skinny-M stream runs sixteen waves per block, with two (M = 32) eight
+    # waves that regroup the token rows through LDS; every epilogue on both
+    H = 4096
     if kind == "rowpar":
         # Z [8, 1024] = Y [8, 4096] . W2 [4096, 1024]: 64 blocks, K = 4096
         w = inputs.Workload(54, "narrow_rowpar", "bf16", M=M, H=1024, F=4096, T=1)
