@@ -50,7 +50,6 @@ struct GemmDev {
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
 typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4v;
-typedef __attribute__((address_space(3))) char lds_char;
 
 // LDS rows hold BK bf16 = CH chunks of 16 B; chunk c of row r sits at slot
 // c ^ swz(r).  The two swizzles make every ds_read_b128 of a fragment (32
@@ -234,11 +233,16 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     for (int i = 0; i < TM; ++i) a_tr[i] = 16 * (((wm * C_::WTM + 32 * i) / 8) ^ (4 * trr)) + tr_lane;
 #pragma unroll
     for (int j = 0; j < TN; ++j) b_tr[j] = 16 * (((wn * C_::WTN + 32 * j) / 8) ^ (4 * trr)) + tr_lane;
+    // The reads index the stage in 8-byte elements (every offset here is a
+    // multiple of 8): formed as byte offsets, the second read of each pair
+    // lost track of which LDS array it reads, and the compiler made it wait
+    // for every global->LDS load in flight, the next slices' included.
     auto tr_frag = [&](const u32x4 *region, int rowbytes, int off, int q) __attribute__((always_inline)) {
-        const lds_char *base = reinterpret_cast<const lds_char *>(LDS_PTR(region));
+        const lds_bf16x4v *b8 = reinterpret_cast<const lds_bf16x4v *>(LDS_PTR(region));
         const int k0 = 16 * q + 8 * fhalf + trr;
-        const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(base + k0 * rowbytes + off));
-        const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(base + (k0 + 4) * rowbytes + off));
+        const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(b8 + ((k0 * rowbytes + off) >> 3)));
+        const bf16x4v hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(b8 + (((k0 + 4) * rowbytes + off) >> 3)));
         return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
 
