@@ -782,8 +782,12 @@ tp_status tp_colpar_bwd(const void *X, const void *W1t, const void *dU_i, float 
             hipSuccess)
             return hip_fail(e, "column-parallel weight-gradient launch");
     }
-    if (db1 && (e = tpk::launch_colsum_bf16(dU_i, Fs, M, Fs, db1 + (int64_t)i * Fs, acc, stream)) != hipSuccess)
-        return hip_fail(e, "bias-gradient launch");
+    if (db1) {
+        const void *x[1] = {dU_i};
+        float *o[1] = {db1 + (int64_t)i * Fs};
+        if ((e = tpk::launch_colsum_bf16(x, 1, Fs, M, Fs, o, acc, stream)) != hipSuccess)
+            return hip_fail(e, "bias-gradient launch");
+    }
     return ok();
 }
 
@@ -956,9 +960,11 @@ tp_status tp_mlp_group_bwd(const void *X, const void *W1t, const void *W2t, void
     w1.K = M;
     if ((e = launch_mfma(w1, wepi, tpk::LAYOUT_AB_KMAJOR, stream)) != hipSuccess)
         return hip_fail(e, "group weight-gradient launch");
-    for (int j = 0; j < T; ++j)
-        if ((e = tpk::launch_colsum_bf16(dU_ws[j], Fs, M, Fs, db1 + (int64_t)j * Fs, acc, stream)) != hipSuccess)
-            return hip_fail(e, "group bias-gradient launch");
+    // db1: the column sums of every shard's dU, one launch
+    float *db1_j[tpk::kMaxPartials];
+    for (int j = 0; j < T; ++j) db1_j[j] = db1 + (int64_t)j * Fs;
+    if ((e = tpk::launch_colsum_bf16(dU_ws, T, Fs, M, Fs, db1_j, acc, stream)) != hipSuccess)
+        return hip_fail(e, "group bias-gradient launch");
     return ok();
 }
 

@@ -90,16 +90,25 @@ hipError_t launch_t(const PartialPtrs &P, const float *residual, float *out, voi
     return hipGetLastError();
 }
 
-// Column sums of a bf16 matrix X [M][N] (row stride ld) in fp32, in a fixed
-// order: a workgroup owns 32 columns; thread t reads 8 of them (16 bytes)
-// from rows t/4, t/4 + 64, t/4 + 128, ... with four loads in flight, and the
-// 64 row-lanes' sums are then added in row-lane order through LDS.
-__global__ void __launch_bounds__(256) colsum_kernel(const __bf16 *X, int64_t ld, int M, int N, float *out,
-                                                     int accumulate)
+// Column sums of bf16 matrices X_j [M][N] (row stride ld), j < batch, into
+// fp32 out_j[N], in a fixed order.  A workgroup owns 64 columns of one matrix,
+// so every row it reads is one whole 128-byte line: thread t reads 8 columns
+// (16 bytes) from rows t/8, t/8 + 64, t/8 + 128, ... with four loads in flight.
+// The 64 row lanes' sums are then added through LDS, eight lanes at a time
+// and the eight group sums in group order.  blockIdx.y picks the matrix, so
+// the T shards of a group fill the chip in one launch.
+struct ColsumPtrs {
+    const __bf16 *x[kMaxPartials];
+    float *out[kMaxPartials];
+};
+
+__global__ void __launch_bounds__(512) colsum_kernel(ColsumPtrs P, int64_t ld, int M, int N, int accumulate)
 {
-    __shared__ float part[64][33];
-    const int t = threadIdx.x, cc = t & 3, rl = t >> 2;
-    const int n0 = blockIdx.x * 32 + 8 * cc;
+    constexpr int RL = 64;   // row lanes
+    __shared__ float part[RL][65];
+    __shared__ float part2[8][64];
+    const int t = threadIdx.x, cc = t & 7, rl = t >> 3;
+    const int n0 = blockIdx.x * 64 + 8 * cc;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
@@ -111,36 +120,51 @@ __global__ void __launch_bounds__(256) colsum_kernel(const __bf16 *X, int64_t ld
         }
     };
     if (n0 < N) {
-        const __bf16 *col = X + n0;
+        const __bf16 *col = P.x[blockIdx.y] + n0;
         int m = rl;
-        for (; m + 3 * 64 < M; m += 4 * 64) {
+        for (; m + 3 * RL < M; m += 4 * RL) {
             u32x4 w[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const u32x4 *>(col + (int64_t)(m + 64 * u) * ld);
+            for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const u32x4 *>(col + (int64_t)(m + RL * u) * ld);
 #pragma unroll
             for (int u = 0; u < 4; ++u) add(w[u]);
         }
-        for (; m < M; m += 64) add(*reinterpret_cast<const u32x4 *>(col + (int64_t)m * ld));
+        for (; m < M; m += RL) add(*reinterpret_cast<const u32x4 *>(col + (int64_t)m * ld));
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[rl][8 * cc + e] = acc[e];
     __syncthreads();
-    if (t < 32) {
-        const int n = blockIdx.x * 32 + t;
+    {
+        const int c = t & 63, grp = t >> 6;   // 8 groups x 64 columns = 512 threads
         float sum = 0.0f;
-        for (int r = 0; r < 64; ++r) sum += part[r][t];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) sum += part[8 * grp + r][c];
+        part2[grp][c] = sum;
+    }
+    __syncthreads();
+    if (t < 64) {
+        const int n = blockIdx.x * 64 + t;
+        float sum = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) sum += part2[g][t];
+        float *out = P.out[blockIdx.y];
         if (n < N) out[n] = accumulate ? out[n] + sum : sum;
     }
 }
 
 }  // namespace
 
-hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t M, int64_t N, float *out, bool accumulate,
-                              hipStream_t s)
+hipError_t launch_colsum_bf16(const void *const *X, int batch, int64_t ld, int64_t M, int64_t N,
+                              float *const *out, bool accumulate, hipStream_t s)
 {
-    const unsigned grid = (unsigned)((N + 31) / 32);
-    hipLaunchKernelGGL(colsum_kernel, dim3(grid), dim3(256), 0, s, static_cast<const __bf16 *>(X), ld, (int)M, (int)N,
-                       out, accumulate ? 1 : 0);
+    if (batch < 1 || batch > kMaxPartials) return hipErrorInvalidValue;
+    ColsumPtrs P{};
+    for (int j = 0; j < batch; ++j) {
+        P.x[j] = static_cast<const __bf16 *>(X[j]);
+        P.out[j] = out[j];
+    }
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)batch);
+    hipLaunchKernelGGL(colsum_kernel, grid, dim3(512), 0, s, P, ld, (int)M, (int)N, accumulate ? 1 : 0);
     return hipGetLastError();
 }
 

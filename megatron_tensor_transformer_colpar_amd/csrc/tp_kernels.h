@@ -89,14 +89,15 @@ struct AttnPlan {
 AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv);
 hipError_t launch_attn_bf16(const AttnArgs &a, int num_cu, hipStream_t s);
 
-// out[n] (+)= sum_m X[m][n] for a bf16 X [M][N] (row stride ld, N and ld
-// multiples of 8), fp32, in a fixed order.
-hipError_t launch_colsum_bf16(const void *X, int64_t ld, int64_t M, int64_t N, float *out, bool accumulate,
-                              hipStream_t s);
 
 // out = (residual ? residual : 0) + sum_j partials[j]; optional bf16 copy,
 // optionally row-RMS-normalised.
 constexpr int kMaxPartials = 8;
+
+// out_j[n] (+)= sum_m X_j[m][n] for bf16 X_j [M][N], j < batch <= kMaxPartials
+// (row stride ld, N and ld multiples of 8), fp32, in a fixed order; one launch.
+hipError_t launch_colsum_bf16(const void *const *X, int batch, int64_t ld, int64_t M, int64_t N,
+                              float *const *out, bool accumulate, hipStream_t s);
 hipError_t launch_shard_reduce(const float *const *partials, int T, const float *residual,
                                float *out, void *out_bf16, int64_t M, int64_t H, bool rms,
                                float eps, hipStream_t s);
