@@ -7,7 +7,7 @@
 // so it is HBM-bound.  Every lane moves 16 bytes per tensor per step, and all
 // T loads of a step are issued before the adds.  The row-normalised variant
 // runs one workgroup per row and reduces the sum of squares with wavefront
-// shuffles, then across the four waves through LDS.
+// shuffles, then across the sixteen waves through LDS.
 #include "device_common.h"
 #include "tp_kernels.h"
 
@@ -49,27 +49,58 @@ __global__ void __launch_bounds__(256) reduce_kernel(PartialPtrs P, const f32x4 
     }
 }
 
+// Row-normalised variant: one workgroup of RMS_THREADS threads per row.  Each
+// pass of a thread covers two 16-byte elements of every tensor, and all
+// 2(T [+1]) loads of a pass are issued before the adds, so a workgroup keeps
+// a whole H = 8192 row (8 partials + residual, 288 KiB) in flight at once:
+// at decode sizes a handful of rows is the whole launch, and its time is the
+// latency of one round of loads (80-layer decode stack at M = 8: 9.3 us with
+// 256 threads and one element per pass, 5.9 us like this).
+constexpr int RMS_THREADS = 1024;
+
 template <int T>
-__global__ void __launch_bounds__(256) reduce_rms_kernel(PartialPtrs P, const f32x4 *residual, f32x4 *out,
-                                                         u32x2 *out_bf16, int64_t h4, float inv_h, float eps)
+__global__ void __launch_bounds__(RMS_THREADS) reduce_rms_kernel(PartialPtrs P, const f32x4 *residual, f32x4 *out,
+                                                                 u32x2 *out_bf16, int64_t h4, float inv_h, float eps)
 {
-    __shared__ float wsum[4];
+    constexpr int NT = RMS_THREADS, NWV = NT / 64;
+    __shared__ float wsum[NWV];
     const int64_t base = (int64_t)blockIdx.x * h4;
     float ss = 0.0f;
-    for (int64_t c = threadIdx.x; c < h4; c += 256) {
-        f32x4 s = sum_partials<T>(P, base + c);
-        if (residual) s = residual[base + c] + s;
-        out[base + c] = s;
-        ss += s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
+    for (int64_t c = threadIdx.x; c < h4; c += 2 * NT) {
+        // the second element of a pass past the row end re-reads the last
+        // element of the row and is not stored
+        const int64_t c2 = c + NT < h4 ? c + NT : h4 - 1;
+        f32x4 v[2][T + 1];
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            v[0][j] = P.p[j][base + c];
+            v[1][j] = P.p[j][base + c2];
+        }
+        if (residual) {
+            v[0][T] = residual[base + c];
+            v[1][T] = residual[base + c2];
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            if (e == 1 && c + NT >= h4) break;
+            f32x4 s = v[e][0];
+#pragma unroll
+            for (int j = 1; j < T; ++j) s += v[e][j];
+            if (residual) s = v[e][T] + s;
+            out[base + (e ? c2 : c)] = s;
+            ss += s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
+        }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
     if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) tot += wsum[w];
     const float r = rsqrtf(tot * inv_h + eps);
     // each thread re-reads only the elements it wrote itself
-    for (int64_t c = threadIdx.x; c < h4; c += 256) out_bf16[base + c] = pack_bf16x4(out[base + c] * r);
+    for (int64_t c = threadIdx.x; c < h4; c += NT) out_bf16[base + c] = pack_bf16x4(out[base + c] * r);
 }
 
 template <int T>
@@ -80,7 +111,7 @@ hipError_t launch_t(const PartialPtrs &P, const float *residual, float *out, voi
     f32x4 *o4 = reinterpret_cast<f32x4 *>(out);
     u32x2 *b4 = static_cast<u32x2 *>(ob);
     if (rms) {
-        hipLaunchKernelGGL(reduce_rms_kernel<T>, dim3((unsigned)M), dim3(256), 0, s, P, r4, o4, b4, H / 4,
+        hipLaunchKernelGGL(reduce_rms_kernel<T>, dim3((unsigned)M), dim3(RMS_THREADS), 0, s, P, r4, o4, b4, H / 4,
                            1.0f / (float)H, eps);
     } else {
         const int64_t n4 = M * H / 4;
