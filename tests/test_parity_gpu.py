@@ -256,16 +256,20 @@ def test_reduce_bf16_copy_is_round_to_nearest_even():
     assert np.array_equal(ob.cpu().view(torch.int16).numpy().view(np.uint16), inputs.f32_to_bf16_bits(host))
 
 
-@pytest.mark.parametrize("H", [64, 8192])
-def test_reduce_rms_copy(H):
+# the row-RMS kernel runs 1024 threads per row, two 16-byte elements per
+# thread and pass: H = 64 leaves most threads idle, 4160 gives a ragged second
+# element, 8192 is exactly one pass, 12288 two passes; in place is how the
+# layer driver calls it (the sum overwrites the residual)
+@pytest.mark.parametrize("H,inplace", [(64, False), (4160, False), (8192, False), (12288, False), (12288, True)])
+def test_reduce_rms_copy(H, inplace):
     M, T = 9, 8
     g = torch.Generator().manual_seed(H)
     P = [torch.randn(M, H, generator=g).cuda() * 50 for _ in range(T)]
     R = torch.randn(M, H, generator=g).cuda()
-    out = torch.empty(M, H, device="cuda")
+    want, wrms = oracle.shard_reduce(np.stack([to_f64(p) for p in P]), to_f64(R), rms_eps=tp.TP_RMS_EPS)
+    out = R if inplace else torch.empty(M, H, device="cuda")
     ob = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
     tp.tp_shard_reduce(P, T, R, out, ob, M, H, tp.TP_REDUCE_RMS_BF16)
-    want, wrms = oracle.shard_reduce(np.stack([to_f64(p) for p in P]), to_f64(R), rms_eps=tp.TP_RMS_EPS)
     assert rel_fro(to_f64(out), want) <= 1e-6
     assert rel_fro(to_f64(ob), wrms) <= TOL["bf16"]
 
