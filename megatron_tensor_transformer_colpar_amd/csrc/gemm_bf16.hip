@@ -21,6 +21,8 @@
 //    lives at slot c ^ swz(r), so fragment reads (32 rows, one chunk each)
 //    spread over all banks.  Rows past M or N read as zero through the
 //    buffer resource, so ragged tiles need no branches in the main loop.
+//  * The fp32 epilogue (row-parallel partials, gradients) goes through LDS,
+//    so each store instruction writes whole 128-byte lines of 8 rows.
 //  * Waits are explicit (vmcnt for the DMA of the slice about to be used,
 //    lgkmcnt(0) so no wave still reads a stage when it is refilled) followed
 //    by a bare s_barrier: a __syncthreads() fence would also drain the
@@ -370,7 +372,42 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         }
         return v;
     };
-    if constexpr (GATED) {
+    if constexpr (EPI == EPI_STORE_F32) {
+        // fp32 output leaves through LDS, one 32x32 accumulator tile at a time
+        // per wave (4 KiB each, inside stage 0), so that every store
+        // instruction writes 8 rows x 128 contiguous bytes, i.e. whole lines.
+        // Stored straight from the accumulators, an instruction wrote 32 bytes
+        // in each of 32 rows; on the 4-shard row-parallel launch at 2048
+        // tokens that took 261 us against 247 us like this.
+        // Rows of the staging tile are 8 chunks of 4 floats; chunk c of row r
+        // sits at slot c ^ swz(r), which keeps both the column-wise write and
+        // the row-wise read conflict-free.  A wave's LDS operations complete
+        // in issue order, so no wait separates its writes from its reads or
+        // one tile's reads from the next tile's writes.
+        static_assert(NW * 32 * 32 * 4 <= STAGE * 16, "epilogue staging area");
+        __syncthreads();   // every wave is done reading the last slice
+        float *const stg = reinterpret_cast<float *>(st0) + wave * 32 * 32;
+        const int mw = m0 + wm * C_::WTM, nw = n0 + wn * C_::WTN;
+        const int rrow = lane >> 3, rch = lane & 7;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<f32x4 *>(stg + frow * 32 + 4 * ((2 * q + fhalf) ^ swz<8>(frow))) =
+                        f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 8 * rr + rrow;
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(stg + r * 32 + 4 * (rch ^ swz<8>(r)));
+                    const int m = mw + 32 * i + r, n = nw + 32 * j + 4 * rch;
+                    if (full || (m < g.M && n < g.N))
+                        *reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n) = x;
+                }
+            }
+        }
+    } else if constexpr (GATED) {
         const __bf16 *const bias2_p = g.bias2[bt];
 #pragma unroll
         for (int j = 0; j < TN / 2; ++j) {
@@ -416,9 +453,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
                     const int n = nb + 8 * q;
                     if (!full && n >= g.N) continue;
                     f32x4 x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    if constexpr (EPI == EPI_STORE_F32) {
-                        *reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n) = x;
-                    } else if constexpr (EPI == EPI_ACC_F32) {
+                    if constexpr (EPI == EPI_ACC_F32) {
                         f32x4 *c = reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n);
                         *c = *c + x;
                     } else if constexpr (epi_act_grad(EPI)) {
