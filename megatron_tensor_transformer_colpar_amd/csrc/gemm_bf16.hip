@@ -21,8 +21,8 @@
 //    lives at slot c ^ swz(r), so fragment reads (32 rows, one chunk each)
 //    spread over all banks.  Rows past M or N read as zero through the
 //    buffer resource, so ragged tiles need no branches in the main loop.
-//  * The fp32 epilogue (row-parallel partials, gradients) goes through LDS,
-//    so each store instruction writes whole 128-byte lines of 8 rows.
+//  * The fp32 and bf16 epilogues (partials, activations, gradients) go
+//    through LDS, so each store instruction writes whole 128-byte lines.
 //  * Waits are explicit (vmcnt for the DMA of the slice about to be used,
 //    lgkmcnt(0) so no wave still reads a stage when it is refilled) followed
 //    by a bare s_barrier: a __syncthreads() fence would also drain the
@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         }
         return v;
     };
-    if constexpr (EPI == EPI_STORE_F32) {
+    if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) {
         // fp32 output leaves through LDS, one 32x32 accumulator tile at a time
         // per wave (4 KiB each, inside stage 0), so that every store
         // instruction writes 8 rows x 128 contiguous bytes, i.e. whole lines.
@@ -402,8 +402,13 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
                     const int r = 8 * rr + rrow;
                     const f32x4 x = *reinterpret_cast<const f32x4 *>(stg + r * 32 + 4 * (rch ^ swz<8>(r)));
                     const int m = mw + 32 * i + r, n = nw + 32 * j + 4 * rch;
-                    if (full || (m < g.M && n < g.N))
-                        *reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n) = x;
+                    if (full || (m < g.M && n < g.N)) {
+                        f32x4 *const c = reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n);
+                        if constexpr (EPI == EPI_ACC_F32)
+                            *c = *c + x;   // accumulate (weight gradients over micro-batches)
+                        else
+                            *c = x;
+                    }
                 }
             }
         }
@@ -438,43 +443,74 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
             }
         }
     } else {
+        // bf16 output (and the kept GeLU input) leaves through LDS like the
+        // fp32 output: a wave stages its 32 x WTN block of one accumulator
+        // row i (TN 16-byte chunks of 8 values per 32 columns; a lane puts
+        // its 4 values of chunk 4j + q into half fhalf of the slot), then
+        // reads it back row-wise, so a store instruction writes 64/CHR rows
+        // x CHR*16 contiguous bytes: whole 128-byte lines when WTN = 64.
+        constexpr int CHR = TN * 4, RPI = 64 / CHR;
+        static_assert(NW * 32 * CHR <= STAGE, "epilogue staging area");
+        __syncthreads();   // every wave is done reading the last slice
+        u32x4 *const stg = st0 + wave * 32 * CHR;
+        const int mw = m0 + wm * C_::WTM, nw = n0 + wn * C_::WTN;
+        f32x4 bias[TN][4];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int nb = n0 + wn * C_::WTN + j * 32 + 4 * fhalf;
-            f32x4 bias[4];
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) bias[q] = epi_has_bias(EPI) ? load_bias(bias_p, nb, q) : f32x4{};
+            for (int q = 0; q < 4; ++q)
+                bias[j][q] = epi_has_bias(EPI) ? load_bias(bias_p, nw + j * 32 + 4 * fhalf, q) : f32x4{};
+        auto put = [&](int j, int q, f32x4 v) __attribute__((always_inline)) {
+            const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+            reinterpret_cast<u32x2 *>(stg + frow * CHR + ((4 * j + q) ^ swz<CHR>(frow)))[fhalf] =
+                __builtin_bit_cast(u32x2, b);
+        };
+        auto drain = [&](__bf16 *dst, int64_t ld, int i) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int m = m0 + wm * C_::WTM + i * 32 + frow;
-                if (!full && m >= g.M) continue;
+            for (int rr = 0; rr < CHR / 2; ++rr) {
+                const int r = RPI * rr + lane / CHR, c = lane % CHR;
+                const u32x4 v = stg[r * CHR + (c ^ swz<CHR>(r))];
+                const int m = mw + 32 * i + r, n = nw + 8 * c;
+                if (full || (m < g.M && n < g.N)) *reinterpret_cast<u32x4 *>(dst + (int64_t)m * ld + n) = v;
+            }
+        };
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = nb + 8 * q;
-                    if (!full && n >= g.N) continue;
-                    f32x4 x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    if constexpr (EPI == EPI_ACC_F32) {
-                        f32x4 *c = reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n);
-                        *c = *c + x;
-                    } else if constexpr (epi_act_grad(EPI)) {
-                        // gradient at the GeLU input: x * g'(u), u the saved GeLU input
-                        const bf16x4 u = *reinterpret_cast<const bf16x4 *>(aux_p + (int64_t)m * g.ldaux + n);
-                        const bf16x4 y = {(__bf16)(x[0] * act_grad<EPI>((float)u[0])),
-                                          (__bf16)(x[1] * act_grad<EPI>((float)u[1])),
-                                          (__bf16)(x[2] * act_grad<EPI>((float)u[2])),
-                                          (__bf16)(x[3] * act_grad<EPI>((float)u[3]))};
-                        *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * ldc + n) = y;
-                    } else {
-                        x += bias[q];
-                        if (aux_p) {   // keep the GeLU input for the backward pass
-                            const bf16x4 u = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-                            *reinterpret_cast<bf16x4 *>(aux_p + (int64_t)m * g.ldaux + n) = u;
-                        }
-                        const bf16x4 y = {(__bf16)act<EPI>(x[0]), (__bf16)act<EPI>(x[1]), (__bf16)act<EPI>(x[2]),
-                                          (__bf16)act<EPI>(x[3])};
-                        *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * ldc + n) = y;
+        for (int i = 0; i < TM; ++i) {
+            const int m = mw + 32 * i + frow;   // this lane's row on the staging side
+            auto xv = [&](int j, int q) __attribute__((always_inline)) {
+                return f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            };
+            if constexpr (epi_act_grad(EPI)) {
+                // gradient at the GeLU input: x * g'(u), u the saved GeLU input
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = nw + j * 32 + 8 * q + 4 * fhalf;
+                        bf16x4 u = {};
+                        if (full || (m < g.M && n < g.N))
+                            u = *reinterpret_cast<const bf16x4 *>(aux_p + (int64_t)m * g.ldaux + n);
+                        const f32x4 x = xv(j, q);
+                        put(j, q, f32x4{x[0] * act_grad<EPI>((float)u[0]), x[1] * act_grad<EPI>((float)u[1]),
+                                        x[2] * act_grad<EPI>((float)u[2]), x[3] * act_grad<EPI>((float)u[3])});
                     }
+                drain(static_cast<__bf16 *>(Cbase), ldc, i);
+            } else {
+                if (aux_p) {   // keep the GeLU input for the backward pass
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) put(j, q, xv(j, q) + bias[j][q]);
+                    drain(aux_p, g.ldaux, i);
                 }
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 x = xv(j, q) + bias[j][q];
+                        put(j, q, f32x4{act<EPI>(x[0]), act<EPI>(x[1]), act<EPI>(x[2]), act<EPI>(x[3])});
+                    }
+                drain(static_cast<__bf16 *>(Cbase), ldc, i);
             }
         }
     }
