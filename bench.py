@@ -7,7 +7,10 @@ with fused bias + GeLU, then row-parallel down-projection into an fp32
 partial, each as one launch over the tiles of all 4 shards) and the
 on-device sum of the 4 partials.  ``value`` is that step's GEMM
 throughput in TFLOP/s (4*M*H*F flops per step; GeLU and the reduce are not
-counted), with every input resident in HBM before timing starts.
+counted), with every input resident in HBM before timing starts.  The K
+timed steps carry HIP events only at their two ends; the same K steps then
+run again with an event before every launch, for the per-kernel durations
+(``kernels``, ``roofline``) and ``ms_per_step_with_kernel_events``.
 
 Also reported on the same JSON line:
   roofline      the dominant kernel's achieved TFLOP/s (algorithmic flops per
@@ -76,6 +79,24 @@ def measured_traffic(kernel_key):
             "profile": rec["profile"]}
 
 
+def warm(torch, f, min_ms=30.0, max_calls=4000):
+    """Untimed warm-up: call f(k) (a section's own launches) until at least
+    min_ms of GPU time has passed.  After the GPU idles for a moment (inputs
+    being generated, a section starting), the first few ms of launches run
+    at a lower clock; a fixed count of a few calls would time that ramp."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    k = 0
+    while True:
+        f(k)
+        k += 1
+        if k % 4 == 0 or k >= max_calls:
+            e1.record()
+            e1.synchronize()
+            if e0.elapsed_time(e1) >= min_ms or k >= max_calls:
+                return k
+
+
 class Timeline:
     """Events recorded between launches on torch's current stream."""
 
@@ -126,18 +147,29 @@ def headline(args, torch, tp, inputs):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, events between launches
-    tl = Timeline(torch)
+    # timed region: K steps with events only at its two ends (an event
+    # recorded between two launches holds the next launch back by a few us,
+    # which is measurement, not work) ...
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    # ... then the same K steps again with an event before every launch, for
+    # each kernel's mean launch duration (the roofline's `achieved`)
+    tl = Timeline(torch)
+    torch.cuda.synchronize()
     tl.mark(None)
     for _ in range(args.steps):
         step(tl)
     tl.mark(None)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = tl.marks[0][1].elapsed_time(tl.marks[-1][1])
-    ms = total_ms / args.steps
+    ms_events = tl.marks[0][1].elapsed_time(tl.marks[-1][1]) / args.steps
     flops_step = 4.0 * M * H * F
     kernels = {}
     for name, d in tl.durations().items():
@@ -152,7 +184,8 @@ def headline(args, torch, tp, inputs):
             entry["bytes_per_launch"] = by
             entry["gbs"] = round(by / (mean * 1e-3) / 1e9, 1)
         kernels[name] = entry
-    log("[bench] headline: %.4f ms/step, %.1f TFLOP/s, wall %.3fs" % (ms, flops_step / (ms * 1e-3) / 1e12, wall))
+    log("[bench] headline: %.4f ms/step, %.1f TFLOP/s, wall %.3fs (%.4f ms/step with an event before every launch)"
+        % (ms, flops_step / (ms * 1e-3) / 1e12, wall, ms_events))
 
     # one rank's own launches (what a single rank's GPU runs): shard 0 alone
     def rank_step(tl):
@@ -177,8 +210,8 @@ def headline(args, torch, tp, inputs):
     # leave the full step's result in Z for the parity check
     step()
     torch.cuda.synchronize()
-    return dict(w=w, ms=ms, flops=flops_step, kernels=kernels, per_rank=per_rank, X=X, W1=W1, b1=b1, W2=W2,
-                Z=Z, wall=wall)
+    return dict(w=w, ms=ms, ms_events=ms_events, flops=flops_step, kernels=kernels, per_rank=per_rank, X=X, W1=W1,
+                b1=b1, W2=W2, Z=Z, wall=wall)
 
 
 def prefill(args, torch, tp):
@@ -199,17 +232,25 @@ def prefill(args, torch, tp):
         if tl: tl.mark("gemm_rowpar_partial")
         tp.tp_rowpar_partial(Y, dW2t, Z, M, H, Fs, 1, 0, tp.TP_BF16, stream)
 
-    for _ in range(3):
+    warm(torch, lambda k: step())
+    n = max(3, args.steps // 5)
+    # the step with events only around the run, then again with an event
+    # before each launch for the per-kernel figures
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
         step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
     tl = Timeline(torch)
     torch.cuda.synchronize()
     tl.mark(None)
-    n = max(3, args.steps // 5)
     for _ in range(n):
         step(tl)
     tl.mark(None)
     torch.cuda.synchronize()
-    ms = tl.marks[0][1].elapsed_time(tl.marks[-1][1]) / n
     fl = 4.0 * M * H * Fs
     out = {"workload": "prefill H=8192 F/T=4096 M=8192 (rank 0)", "ms_per_call": round(ms, 4),
            "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
@@ -233,8 +274,7 @@ def variants(args, torch, tp):
         return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
 
     def timed(f, n):
-        for k in range(3):
-            f(k)
+        warm(torch, f)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -289,8 +329,7 @@ def attention(args, torch, tp):
         return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
 
     def timed(f, n):
-        for k in range(3):
-            f(k)
+        warm(torch, f)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -406,8 +445,7 @@ def backward(args, torch, tp):
         ms = {}
         n = max(3, args.steps // 5)
         for name, f in ops:
-            for _ in range(2):
-                f()
+            warm(torch, lambda k: f())
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             e0.record()
@@ -453,8 +491,7 @@ def backward(args, torch, tp):
     ms = {}
     n = max(3, args.steps // 5)
     for name, f in (("forward_train", fwd), ("backward", bwd), ("dX_reduce", red)):
-        for _ in range(2):
-            f()
+        warm(torch, lambda k: f())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -487,8 +524,7 @@ def hipblaslt_context(args, torch, tp):
     stream = torch.cuda.current_stream().cuda_stream
 
     def timed(f, reps=20):
-        for _ in range(3):
-            f()
+        warm(torch, lambda k: f())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
@@ -550,8 +586,7 @@ def decode(args, torch, tp):
             if tl: tl.mark("outproj")
             tp.tp_rowpar_partial(ctx, s["Wot"], O, M, H, As, 1, 0, tp.TP_BF16, stream)
 
-        for k in range(2 * R):
-            step(sets[k % R])
+        warm(torch, lambda k: step(sets[k % R]))
         n = max(2 * R, args.steps)
         # the step itself, with events only around the whole run (an event
         # between two launches adds a gap of its own) ...
@@ -697,7 +732,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # 10 warm-up steps (5 ms) leave the first timed steps at a lower clock:
+    # 0.540 against 0.508 ms/step after 100 or more (measured on MI355X)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-sets", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -748,7 +785,8 @@ def main():
            "data": "synthetic: seeded N(0,1) activations, N(0,0.02) weights, N(0,0.01) bias (bf16 RNE)",
            "config": {"workload": "gpt_block_shard: all 4 TP shards + on-device reduce", "M": w.M, "H": w.H,
                       "F": w.F, "T": w.T, "parallelism": "tp4 emulated on 1 GPU"},
-           "roofline": roof, "kernels": kernels, "per_rank": hl["per_rank"]}
+           "roofline": roof, "kernels": kernels, "ms_per_step_with_kernel_events": round(hl["ms_events"], 4),
+           "per_rank": hl["per_rank"]}
     sections = set() if args.no_extras else set(x for x in args.sections.split(",") if x)
     if "prefill" in sections:
         rec["prefill"] = prefill(args, torch, tp)
