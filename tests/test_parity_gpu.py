@@ -107,6 +107,36 @@ def test_prefill_full_size_sampled_rows():
     assert ey <= TOL["bf16"] and ez <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("train", [False, True])
+def test_ragged_tokens_on_the_largest_tile(train):
+    # 4196 tokens (16 whole 256-row tiles and 100 rows) on H=4096 with a
+    # 4096-wide shard: 272 tiles, so both projections run the 256x256 tile,
+    # whose epilogues stage through LDS and store a partial last tile row;
+    # the training forward also keeps the GeLU input through the same path
+    M, H, Fs = 4196, 4096, 4096
+    w = inputs.Workload(23, "ragged_big_tile", "bf16", M=M, H=H, F=Fs, T=1)
+    X, W1, b1, W2 = inputs.mlp_inputs(w)
+    dev = DeviceMLP(X, W1, b1, W2)
+    if train:
+        Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+        U = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+        tp.tp_colpar_act_train(dev.X, dev.W1t, dev.b1, Y, U, M, H, Fs, 1, 0)
+        Z = torch.empty(M, H, dtype=torch.float32, device="cuda")
+        tp.tp_rowpar_partial(Y, dev.W2t, Z, M, H, Fs, 1, 0, tp.TP_BF16)
+    else:
+        Y, Z = dev.shard(1, 0, use_fused=False)
+    torch.cuda.synchronize()
+    rows = np.array([0, 255, 256, 4095, 4096, 4150, 4195])
+    Yr, Zr = oracle.mlp_shard(X.f64[rows], W1.f64, b1.f64, W2.f64, 1, 0)
+    ey, ez = rel_fro(to_f64(Y)[rows], Yr), rel_fro(to_f64(Z)[rows], Zr)
+    print("  Y %.2e  Z %.2e" % (ey, ez))
+    assert ey <= TOL["bf16"] and ez <= TOL["bf16"]
+    if train:
+        eu = rel_fro(to_f64(U)[rows], oracle.colpar_linear(X.f64[rows], W1.f64, b1.f64, 1, 0))
+        print("  U %.2e" % eu)
+        assert eu <= TOL["bf16"]
+
+
 def test_full_matrix_and_rank_local_calls_agree_bitwise():
     # Shard i of the full W1^T/W2^T (F, T, i) is the same computation as the
     # stand-alone shard matrices (F/T, 1, 0); first and last shard.
