@@ -476,20 +476,36 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         };
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int m = mw + 32 * i + frow;   // this lane's row on the staging side
             auto xv = [&](int j, int q) __attribute__((always_inline)) {
                 return f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
             };
             if constexpr (epi_act_grad(EPI)) {
                 // gradient at the GeLU input: x * g'(u), u the saved GeLU input
+                // u's rows arrive the way the output leaves: whole lines,
+                // row-wise into the slot, then each lane takes its values
+                // (read straight into the accumulator layout, a load touched
+                // 16 bytes in each of 32 rows; dU at 2048 tokens 69.6 -> 68.7 us)
+                bf16x4 uv[TN][4];
+#pragma unroll
+                for (int rr = 0; rr < CHR / 2; ++rr) {
+                    const int r = RPI * rr + lane / CHR, c = lane % CHR;
+                    const int mr = mw + 32 * i + r, n = nw + 8 * c;
+                    u32x4 v = {};
+                    if (full || (mr < g.M && n < g.N))
+                        v = *reinterpret_cast<const u32x4 *>(aux_p + (int64_t)mr * g.ldaux + n);
+                    stg[r * CHR + (c ^ swz<CHR>(r))] = v;
+                }
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        uv[j][q] = __builtin_bit_cast(
+                            bf16x4, reinterpret_cast<const u32x2 *>(stg + frow * CHR + ((4 * j + q) ^ swz<CHR>(frow)))[fhalf]);
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int n = nw + j * 32 + 8 * q + 4 * fhalf;
-                        bf16x4 u = {};
-                        if (full || (m < g.M && n < g.N))
-                            u = *reinterpret_cast<const bf16x4 *>(aux_p + (int64_t)m * g.ldaux + n);
+                        const bf16x4 u = uv[j][q];
                         const f32x4 x = xv(j, q);
                         put(j, q, f32x4{x[0] * act_grad<EPI>((float)u[0]), x[1] * act_grad<EPI>((float)u[1]),
                                         x[2] * act_grad<EPI>((float)u[2]), x[3] * act_grad<EPI>((float)u[3])});
