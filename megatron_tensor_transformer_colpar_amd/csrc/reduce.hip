@@ -66,6 +66,7 @@ __global__ void __launch_bounds__(RMS_THREADS) reduce_rms_kernel(PartialPtrs P, 
     __shared__ float wsum[NWV];
     const int64_t base = (int64_t)blockIdx.x * h4;
     float ss = 0.0f;
+    f32x4 keep[2] = {};   // a row of one pass keeps its sums here for the bf16 copy
     for (int64_t c = threadIdx.x; c < h4; c += 2 * NT) {
         // the second element of a pass past the row end re-reads the last
         // element of the row and is not stored
@@ -88,6 +89,7 @@ __global__ void __launch_bounds__(RMS_THREADS) reduce_rms_kernel(PartialPtrs P, 
             for (int j = 1; j < T; ++j) s += v[e][j];
             if (residual) s = v[e][T] + s;
             out[base + (e ? c2 : c)] = s;
+            keep[e] = s;
             ss += s[0] * s[0] + s[1] * s[1] + s[2] * s[2] + s[3] * s[3];
         }
     }
@@ -99,6 +101,12 @@ __global__ void __launch_bounds__(RMS_THREADS) reduce_rms_kernel(PartialPtrs P, 
 #pragma unroll
     for (int w = 0; w < NWV; ++w) tot += wsum[w];
     const float r = rsqrtf(tot * inv_h + eps);
+    if (h4 <= 2 * NT) {   // one pass (H <= 8192): the sums are still in registers
+        const int64_t c = threadIdx.x;
+        if (c < h4) out_bf16[base + c] = pack_bf16x4(keep[0] * r);
+        if (c + NT < h4) out_bf16[base + c + NT] = pack_bf16x4(keep[1] * r);
+        return;
+    }
     // each thread re-reads only the elements it wrote itself
     for (int64_t c = threadIdx.x; c < h4; c += NT) out_bf16[base + c] = pack_bf16x4(out[base + c] * r);
 }
