@@ -361,8 +361,9 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 
     // epilogue: element v of accumulator (i, j) is C[m][n] with
     //   m = tile row base + lane%32,  n = tile column base + 8*(v/4) + 4*(lane/32) + v%4,
-    // so each lane owns runs of 4 consecutive columns: one 16-byte fp32
-    // store or one 8-byte bf16 store per run.
+    // so each lane owns runs of 4 consecutive columns.  The fp32 and plain
+    // bf16 epilogues regroup those runs through LDS into whole-line stores;
+    // the gated one stores each run (8 bytes) directly.
     const bool full = (m0 + BM <= g.M) && (n0 + BNO <= g.N);
     auto load_bias = [&](const __bf16 *bp, int nb, int q) __attribute__((always_inline)) {
         f32x4 v = f32x4{};
