@@ -185,6 +185,23 @@ def test_decode_full_size_mlp_and_outproj(M):
     assert max(e) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("M", [17, 32])
+def test_decode_two_token_tiles_full_width(M):
+    # two token tiles (the token rows regrouped through LDS like the weights)
+    # on a full-width rank share, H=8192, F/T=4096; M = 17 leaves the second
+    # tile with a single token
+    H, Fs = 8192, 4096
+    w = inputs.Workload(24, "decode_two_tiles", "bf16", M=M, H=H, F=Fs, T=1)
+    X, W1, b1, W2 = inputs.mlp_inputs(w)
+    dev = DeviceMLP(X, W1, b1, W2)
+    Y, Z = dev.shard(1, 0, use_fused=False)
+    torch.cuda.synchronize()
+    Yr, Zr = oracle.mlp_shard(X.f64, W1.f64, b1.f64, W2.f64, 1, 0)
+    ey, ez = rel_fro(to_f64(Y), Yr), rel_fro(to_f64(Z), Zr)
+    print("  Y %.2e  Z %.2e" % (ey, ez))
+    assert ey <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
 def test_outproj_head_shards_sum_to_full_projection():
     # Head-sharded out-projection: T=8 ranks with the full W_o^T [H, A]; the
     # reduced partials equal ctx . W_o over all heads.
