@@ -1,6 +1,6 @@
 """Host logic of bench.py, on the CPU: the one-GPU guard exits before any GPU
-work, and the committed HBM traffic record is used only while the kernel
-source it was measured on is unchanged."""
+work, the committed HBM traffic record is used only while the kernel source
+it was measured on is unchanged, and the warm-up runs for its GPU time."""
 import json
 import os
 import subprocess
@@ -51,3 +51,50 @@ def test_stale_or_missing_traffic_record_reads_as_none(tmp_path, monkeypatch):
 def test_cpu_model_is_a_string_or_none():
     m = bench.cpu_model()
     assert m is None or (isinstance(m, str) and m)
+
+
+class _FakeClockTorch:
+    """Stands in for torch in bench.warm(): every launch advances a GPU clock
+    by a fixed time, and events read that clock."""
+
+    def __init__(self, us_per_call):
+        self.now_ms = 0.0
+        self.us = us_per_call
+        outer = self
+
+        class Event:
+            def __init__(self, enable_timing=False):
+                self.t = None
+
+            def record(self):
+                self.t = outer.now_ms
+
+            def synchronize(self):
+                pass
+
+            def elapsed_time(self, other):
+                return other.t - self.t
+
+        class _Cuda:
+            pass
+
+        self.cuda = _Cuda()
+        self.cuda.Event = Event
+
+    def launch(self, k):
+        self.now_ms += self.us / 1000.0
+
+
+@pytest.mark.parametrize("us, calls", [(500.0, 60), (31.0, 968), (1e4, 4)])
+def test_warm_up_runs_for_at_least_its_gpu_time(us, calls):
+    # warm() keeps calling the section's launches until 30 ms of GPU time
+    # have passed, checking every 4 calls
+    t = _FakeClockTorch(us)
+    n = bench.warm(t, t.launch)
+    assert n == calls
+    assert t.now_ms >= 30.0
+
+
+def test_warm_up_stops_at_its_call_limit():
+    t = _FakeClockTorch(0.001)
+    assert bench.warm(t, t.launch, max_calls=100) == 100
