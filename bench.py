@@ -1,41 +1,46 @@
 #!/usr/bin/env python3
 """Benchmark of one tensor-parallel rank's share of a Megatron MLP block on MI355X.
 
-Headline step (the GPT-style block shard): bf16, H=4096, F=16384, T=4,
-M=2048 tokens; every step runs all 4 shards (column-parallel up-projection
-with fused bias + GeLU, then row-parallel down-projection into an fp32
-partial, each as one launch over the tiles of all 4 shards) and the
-on-device sum of the 4 partials.  ``value`` is that step's GEMM
-throughput in TFLOP/s (4*M*H*F flops per step; GeLU and the reduce are not
-counted), with every input resident in HBM before timing starts.  The K
-timed steps carry HIP events only at their two ends; the same K steps then
-run again with an event before every launch, for the per-kernel durations
-(``kernels``, ``roofline``) and ``ms_per_step_with_kernel_events``.
+Headline step (the pages' prefill shape, per rank): bf16, H=8192, F=32768,
+T=8, rank 0's own weight blocks (F/T=4096), M=8192 tokens (4 sequences of
+2048).  One step is the rank's column-parallel up-projection with fused
+bias + GeLU (one launch) and its row-parallel down-projection into an fp32
+partial (one launch).  ``value`` is that step's GEMM throughput in TFLOP/s
+(4*M*H*F/T flops per step; GeLU is not counted), with every input resident
+in HBM before timing starts.  Inputs are the seeded host draws the parity
+tests use (N(0,1) tokens, N(0,0.02) weights, N(0,0.01) bias, bf16 RNE).
+
+Timing: the headline warms up for at least 200 ms of GPU time (and at least
+--warmup steps), then the K timed steps carry HIP events only at their two
+ends (``ms_per_step``, ``value``); then 20 or more trials of 5 steps each
+give the median and spread (``trials``); then K more steps with an event
+before every launch give each kernel's mean duration (``kernels``) and the
+roofline's ``achieved``.
 
 Also reported on the same JSON line:
-  roofline      the dominant kernel's achieved TFLOP/s (algorithmic flops per
-                launch / mean launch time from HIP events over the timed
-                region) against the 2.5 PFLOP/s dense-bf16 MFMA peak
-  per_rank      one shard's own two launches (what one rank's GPU runs)
-  prefill       rank 0's shard at H=8192, F=32768, T=8, M=8192 (TFLOP/s)
-  decode        rank 0's MLP shard + attention out-projection shard at
-                H=8192, F/T=4096, A/T=1024, M in {1, 8, 32}, rotating over
-                weight sets larger than the last-level cache (HBM GB/s)
+  roofline      the dominant kernel's algorithmic TFLOP/s (flops per launch /
+                mean launch duration from HIP events on the launch stream)
+                against the 2.5 PFLOP/s dense-bf16 MFMA peak, with its HBM
+                traffic from the committed rocprofv3 counter runs
+  decode        rank 0's MLP shard + attention out-projection shard at the
+                pages' decode shape (H=8192, F/T=4096, A/T=1024, M in
+                {1, 8, 32}), rotating over weight sets larger than the
+                last-level cache: HBM GB/s and fraction of 8 TB/s, with the
+                rank's all-reduce ring volume for context
+  gpt_block_shard  the GPT-style block (H=4096, F=16384, T=4, M=2048): all 4
+                shards in one launch per projection and the on-device sum
   stack80       80 layers (H=8192, F=32768, A=8192, T=8, whole group per
                 layer) at decode M=8 (weight GB/s) and prefill M=4096 (TFLOP/s)
-  variants      rank 0's exact-GeLU and gated Gate/Up first layer: prefill
-                (TFLOP/s) and gated decode at M=8 (weight GB/s)
-  attention     rank 0's attention front half (8 heads of 128, H=8192):
-                prefill of 4 x 2048 tokens (Q/K/V projection, causal
-                attention, out-projection; TFLOP/s) and decode of M in
-                {1, 8, 32} sequences over 2048 cached positions (GB/s)
-  backward      rank 0's backward pass (training forward, dU with GeLU', dX,
-                dW1, dW2, db1) at the 2048-token block and 8192-token
-                prefill shapes (TFLOP/s; GB/s for db1)
+  variants      rank 0's exact-GeLU and gated Gate/Up first layer
+  attention     rank 0's attention front half (Q/K/V projection, core, cache)
+  backward      rank 0's backward pass
   hipblaslt_context  the column-parallel launches next to torch.matmul
                 (hipBLASLt) on the same shapes, same GPU, same run
-  cpu_baseline  the fp64 oracle on a bounded sample of the headline rows
-  parity        the sampled rows of the last step against the oracle
+  cpu_baseline  the fp64 oracle on a bounded sample of the headline's token
+                rows (extrapolated to all rows, labelled), and on the whole
+                decode step at M = 32
+  parity        the headline's sampled rows and the decode step's outputs
+                against the oracle
 
 Only one GPU is used: ``--gpus`` above 1 is refused.
 """
@@ -79,11 +84,12 @@ def measured_traffic(kernel_key):
             "profile": rec["profile"]}
 
 
-def warm(torch, f, min_ms=30.0, max_calls=4000):
+def warm(torch, f, min_ms=30.0, max_calls=4000, min_calls=0):
     """Untimed warm-up: call f(k) (a section's own launches) until at least
-    min_ms of GPU time has passed.  After the GPU idles for a moment (inputs
-    being generated, a section starting), the first few ms of launches run
-    at a lower clock; a fixed count of a few calls would time that ramp."""
+    min_ms of GPU time has passed and at least min_calls calls were made.
+    After the GPU idles for a moment (inputs being generated, a section
+    starting), the first few ms of launches run at a lower clock; a fixed
+    count of a few calls would time that ramp."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     k = 0
@@ -93,7 +99,7 @@ def warm(torch, f, min_ms=30.0, max_calls=4000):
         if k % 4 == 0 or k >= max_calls:
             e1.record()
             e1.synchronize()
-            if e0.elapsed_time(e1) >= min_ms or k >= max_calls:
+            if (e0.elapsed_time(e1) >= min_ms and k >= min_calls) or k >= max_calls:
                 return k
 
 
@@ -118,7 +124,95 @@ class Timeline:
         return out
 
 
-def headline(args, torch, tp, inputs):
+def trials(torch, f, n_trials=20, per=5):
+    """Median and spread of n_trials runs of `per` calls of f, each run timed
+    with HIP events at its two ends only (ms per call)."""
+    ts = []
+    for _ in range(n_trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(per):
+            f()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) / per)
+    ts.sort()
+    q = lambda p: ts[min(len(ts) - 1, int(round(p * (len(ts) - 1))))]
+    return {"trials": n_trials, "calls_per_trial": per, "median_ms": round(q(0.5), 5), "p10_ms": round(q(0.1), 5),
+            "p90_ms": round(q(0.9), 5), "min_ms": round(ts[0], 5), "max_ms": round(ts[-1], 5)}
+
+
+def prefill_headline(args, torch, tp, inputs):
+    """Rank 0's MLP share at the pages' prefill shape (H=8192, F=32768, T=8,
+    F/T=4096, M=8192), on the seeded host inputs of the parity tests."""
+    w = inputs.WORKLOADS["prefill"]
+    M, H, Fs = w.M, w.H, w.F // w.T
+    log("[bench] generating %s inputs (M=%d H=%d F/T=%d, rank 0)" % (w.name, M, H, Fs))
+    X, W1, b1, W2 = inputs.mlp_inputs(w, shard_only=0)
+    dX, dW1t, db1, dW2t = X.torch(), W1.transposed().torch(), b1.torch(), W2.transposed().torch()
+    Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    BF = tp.TP_BF16
+
+    # one step = rank 0's column-parallel GEMM with bias + GeLU, then its
+    # row-parallel GEMM into the fp32 partial (rank-local weights: F := F/T, T := 1)
+    def step(tl=None):
+        if tl: tl.mark("gemm_up_gelu")
+        tp.tp_colpar_gelu(dX, dW1t, db1, Y, M, H, Fs, 1, 0, BF, stream)
+        if tl: tl.mark("gemm_rowpar_partial")
+        tp.tp_rowpar_partial(Y, dW2t, Z, M, H, Fs, 1, 0, BF, stream)
+
+    # warm-up: at least --warmup steps and at least 200 ms of GPU time (the
+    # clock settles under the power cap only after sustained matrix work)
+    nwarm = warm(torch, lambda k: step(), min_ms=200.0, min_calls=args.warmup)
+    log("[bench] warm-up: %d steps" % nwarm)
+
+    # timed region: K steps with events only at its two ends (an event
+    # recorded between two launches holds the next launch back by a few us)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    # median and spread over 20 trials of 5 steps
+    tri = trials(torch, step)
+    # the same K steps with an event before every launch, for each kernel's
+    # mean launch duration (the roofline's `achieved`)
+    tl = Timeline(torch)
+    torch.cuda.synchronize()
+    tl.mark(None)
+    for _ in range(args.steps):
+        step(tl)
+    tl.mark(None)
+    torch.cuda.synchronize()
+    ms_events = tl.marks[0][1].elapsed_time(tl.marks[-1][1]) / args.steps
+    flops_step = 4.0 * M * H * Fs
+    alg_bytes = {"gemm_up_gelu": 2.0 * (M * H + Fs * H + Fs) + 2.0 * M * Fs,
+                 "gemm_rowpar_partial": 2.0 * (M * Fs + H * Fs) + 4.0 * M * H}
+    kernels = {}
+    for name, d in tl.durations().items():
+        mean = sum(d) / len(d)
+        fl = 2.0 * M * H * Fs
+        kernels[name] = {"launches": len(d), "mean_us": round(mean * 1e3, 2), "flops_per_launch": fl,
+                         "algorithmic_bytes_per_launch": alg_bytes[name],
+                         "tflops": round(fl / (mean * 1e-3) / 1e12, 1)}
+    log("[bench] prefill headline: %.4f ms/step, %.1f TFLOP/s (median of %d trials %.4f ms), wall %.3fs "
+        "(%.4f ms/step with an event before every launch)"
+        % (ms, flops_step / (ms * 1e-3) / 1e12, tri["trials"], tri["median_ms"], wall, ms_events))
+    # leave one step's result in Y and Z for the parity check
+    step()
+    torch.cuda.synchronize()
+    return dict(w=w, ms=ms, ms_events=ms_events, flops=flops_step, kernels=kernels, trials=tri, X=X, W1=W1,
+                b1=b1, W2=W2, Y=Y, Z=Z, wall=wall, warmup_steps=nwarm)
+
+
+def gpt_block_shard(args, torch, tp, inputs):
     w = inputs.WORKLOADS["gpt_block_shard"]
     M, H, F, T = w.M, w.H, w.F, w.T
     Fs = F // T
@@ -142,10 +236,7 @@ def headline(args, torch, tp, inputs):
         if tl: tl.mark("shard_reduce")
         tp.tp_shard_reduce(zarr, T, None, Z, None, M, H, 0, stream)
 
-    log("[bench] warmup %d steps" % args.warmup)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm(torch, lambda k: step(), min_ms=100.0)
 
     # timed region: K steps with events only at its two ends (an event
     # recorded between two launches holds the next launch back by a few us,
@@ -184,8 +275,8 @@ def headline(args, torch, tp, inputs):
             entry["bytes_per_launch"] = by
             entry["gbs"] = round(by / (mean * 1e-3) / 1e9, 1)
         kernels[name] = entry
-    log("[bench] headline: %.4f ms/step, %.1f TFLOP/s, wall %.3fs (%.4f ms/step with an event before every launch)"
-        % (ms, flops_step / (ms * 1e-3) / 1e12, wall, ms_events))
+    log("[bench] gpt_block_shard: %.4f ms/step, %.1f TFLOP/s, wall %.3fs (%.4f ms/step with an event before every "
+        "launch)" % (ms, flops_step / (ms * 1e-3) / 1e12, wall, ms_events))
 
     # one rank's own launches (what a single rank's GPU runs): shard 0 alone
     def rank_step(tl):
@@ -207,59 +298,10 @@ def headline(args, torch, tp, inputs):
                 "up_us": round(d2["up"] * 1e3, 2), "down_us": round(d2["down"] * 1e3, 2),
                 "up_tflops": round(fl / (d2["up"] * 1e-3) / 1e12, 1),
                 "down_tflops": round(fl / (d2["down"] * 1e-3) / 1e12, 1)}
-    # leave the full step's result in Z for the parity check
-    step()
-    torch.cuda.synchronize()
-    return dict(w=w, ms=ms, ms_events=ms_events, flops=flops_step, kernels=kernels, per_rank=per_rank, X=X, W1=W1,
-                b1=b1, W2=W2, Z=Z, wall=wall)
-
-
-def prefill(args, torch, tp):
-    # rank 0's own weight blocks (F := F/T, T := 1): H=8192, F/T=4096, M=8192
-    M, H, Fs = 8192, 8192, 4096
-    g = torch.Generator(device="cuda").manual_seed(4)
-    dX = torch.randn(M, H, generator=g, device="cuda").to(torch.bfloat16)
-    dW1t = (torch.randn(Fs, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-    db1 = (torch.randn(Fs, generator=g, device="cuda") * 0.01).to(torch.bfloat16)
-    dW2t = (torch.randn(H, Fs, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-    Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
-    Z = torch.empty(M, H, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream().cuda_stream
-
-    def step(tl=None):
-        if tl: tl.mark("gemm_up_gelu")
-        tp.tp_colpar_gelu(dX, dW1t, db1, Y, M, H, Fs, 1, 0, tp.TP_BF16, stream)
-        if tl: tl.mark("gemm_rowpar_partial")
-        tp.tp_rowpar_partial(Y, dW2t, Z, M, H, Fs, 1, 0, tp.TP_BF16, stream)
-
-    warm(torch, lambda k: step())
-    n = max(3, args.steps // 5)
-    # the step with events only around the run, then again with an event
-    # before each launch for the per-kernel figures
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(n):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
-    tl = Timeline(torch)
-    torch.cuda.synchronize()
-    tl.mark(None)
-    for _ in range(n):
-        step(tl)
-    tl.mark(None)
-    torch.cuda.synchronize()
-    fl = 4.0 * M * H * Fs
-    out = {"workload": "prefill H=8192 F/T=4096 M=8192 (rank 0)", "ms_per_call": round(ms, 4),
-           "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-           "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    for name, d in tl.durations().items():
-        mean = sum(d) / len(d)
-        out[name + "_tflops"] = round(2.0 * M * H * Fs / (mean * 1e-3) / 1e12, 1)
-    log("[bench] prefill: %s" % out)
-    return out
+    t = flops_step / (ms * 1e-3) / 1e12
+    return {"workload": "gpt_block_shard: all %d TP shards + on-device reduce, M=%d H=%d F=%d" % (T, M, H, F),
+            "ms_per_step": round(ms, 4), "tflops": round(t, 1), "frac": round(t / PEAK_BF16_TFLOPS, 4),
+            "ms_per_step_with_kernel_events": round(ms_events, 4), "kernels": kernels, "per_rank": per_rank}
 
 
 def variants(args, torch, tp):
@@ -557,34 +599,42 @@ def hipblaslt_context(args, torch, tp):
     return out
 
 
-def decode(args, torch, tp):
-    # rank 0 at H=8192, F/T=4096, A/T=1024; R weight sets rotate so that every
-    # call streams its weights from HBM (R * 144 MiB is > 4x the 256 MB MALL).
-    H, Fs, As, R = 8192, 4096, 1024, args.decode_sets
+def decode(args, torch, tp, inputs):
+    """Rank 0's decode step at the pages' decode shape: H=8192, F/T=4096,
+    A/T=1024 (8 heads of 128), M in {1, 8, 32} tokens: the MLP shard
+    (column-parallel up-projection with bias + GeLU, row-parallel partial)
+    and the head-sharded out-projection partial.  R weight sets rotate so
+    that every call streams its weights from HBM (R * 144 MiB is more than
+    4x the 256 MB last-level cache); set 0 is the seeded host draw of the
+    parity tests, and its outputs are kept for the oracle check."""
+    w = inputs.WORKLOADS["decode"]
+    H, Fs, As, R = w.H, w.F // w.T, w.A // w.T, args.decode_sets
+    X, W1, b1, W2 = inputs.mlp_inputs(w, shard_only=0)          # X: 32 token rows
+    ctx, Wo = inputs.outproj_inputs(w, shard=0)
+    host = dict(X=X, W1=W1, b1=b1, W2=W2, ctx=ctx, Wo=Wo)
     g = torch.Generator(device="cuda").manual_seed(3)
-    sets = []
-    for _ in range(R):
+    sets = [dict(W1t=W1.transposed().torch(), b1=b1.torch(), W2t=W2.transposed().torch(), Wot=Wo.transposed().torch())]
+    for _ in range(R - 1):
         sets.append(dict(
             W1t=(torch.randn(Fs, H, generator=g, device="cuda") * 0.02).to(torch.bfloat16),
             b1=(torch.randn(Fs, generator=g, device="cuda") * 0.01).to(torch.bfloat16),
             W2t=(torch.randn(H, Fs, generator=g, device="cuda") * 0.02).to(torch.bfloat16),
             Wot=(torch.randn(H, As, generator=g, device="cuda") * 0.02).to(torch.bfloat16)))
     stream = torch.cuda.current_stream().cuda_stream
-    res = {}
+    dX, dctx = X.torch(), ctx.torch()
+    res, outs = {}, {}
     for M in (1, 8, 32):
-        X = torch.randn(M, H, generator=g, device="cuda").to(torch.bfloat16)
-        ctx = torch.randn(M, As, generator=g, device="cuda").to(torch.bfloat16)
         Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
         Z = torch.empty(M, H, dtype=torch.float32, device="cuda")
         O = torch.empty(M, H, dtype=torch.float32, device="cuda")
 
         def step(s, tl=None):
             if tl: tl.mark("up")
-            tp.tp_colpar_gelu(X, s["W1t"], s["b1"], Y, M, H, Fs, 1, 0, tp.TP_BF16, stream)
+            tp.tp_colpar_gelu(dX, s["W1t"], s["b1"], Y, M, H, Fs, 1, 0, tp.TP_BF16, stream)
             if tl: tl.mark("down")
             tp.tp_rowpar_partial(Y, s["W2t"], Z, M, H, Fs, 1, 0, tp.TP_BF16, stream)
             if tl: tl.mark("outproj")
-            tp.tp_rowpar_partial(ctx, s["Wot"], O, M, H, As, 1, 0, tp.TP_BF16, stream)
+            tp.tp_rowpar_partial(dctx, s["Wot"], O, M, H, As, 1, 0, tp.TP_BF16, stream)
 
         warm(torch, lambda k: step(sets[k % R]))
         n = max(2 * R, args.steps)
@@ -598,6 +648,12 @@ def decode(args, torch, tp):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / n
+        ctr = [0]
+
+        def rotating():
+            step(sets[ctr[0] % R])
+            ctr[0] += 1
+        tri = trials(torch, rotating, n_trials=20, per=R)
         # ... and a second run with an event before each launch for the
         # per-kernel durations
         tl = Timeline(torch)
@@ -609,16 +665,32 @@ def decode(args, torch, tp):
         torch.cuda.synchronize()
         mlp_bytes = 2.0 * (Fs * H * 2 + Fs) + M * H * 2 + M * H * 4
         op_bytes = 2.0 * H * As + M * As * 2 + M * H * 4
+        by = mlp_bytes + op_bytes
         d = {k: sum(v) / len(v) for k, v in tl.durations().items()}
-        e = {"us_per_step": round(ms * 1e3, 2),
-             "gbs": round((mlp_bytes + op_bytes) / (ms * 1e-3) / 1e9, 1),
-             "frac": round((mlp_bytes + op_bytes) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        e = {"us_per_step": round(ms * 1e3, 2), "bytes_per_step": by,
+             "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+             "frac": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+             "median_us": round(tri["median_ms"] * 1e3, 2),
+             "median_frac": round(by / (tri["median_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+             "p10_us": round(tri["p10_ms"] * 1e3, 2), "p90_us": round(tri["p90_ms"] * 1e3, 2),
+             "trials": tri["trials"],
              "up_us": round(d["up"] * 1e3, 2), "down_us": round(d["down"] * 1e3, 2),
              "outproj_us": round(d["outproj"] * 1e3, 2),
              "mlp_kernels_gbs": round(mlp_bytes / ((d["up"] + d["down"]) * 1e-3) / 1e9, 1)}
         res["M=%d" % M] = e
         log("[bench] decode M=%d: %s" % (M, e))
-    return res
+        # the host set's outputs for the oracle check
+        step(sets[0])
+        torch.cuda.synchronize()
+        outs[M] = (Y.clone(), Z.clone(), O.clone())
+    # context: what the rank's two all-reduces per layer would move on a real
+    # TP group (ring, bf16 payload), per decode step
+    from megatron_tensor_transformer_colpar_amd import comm_volume as cv
+    res["allreduce_ring_bytes_per_rank"] = {"M=%d" % M: int(2 * cv.ring_allreduce_bytes_per_rank(H, 2, w.T, tokens=M))
+                                            for M in (1, 8, 32)}
+    res["workload"] = ("rank 0 of T=8: H=8192, F/T=4096, A/T=1024; MLP shard + head-sharded out-projection; "
+                       "%d rotating weight sets" % R)
+    return res, dict(host, outs=outs)
 
 
 def stack80(args, torch, tp):
@@ -667,9 +739,12 @@ def stack80(args, torch, tp):
         e = {"steps": steps, "ms_per_step_group": round(ms, 3), "ms_per_step_per_rank_share": round(ms / T, 3),
              "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
         if M == 8:
+            from megatron_tensor_transformer_colpar_amd import comm_volume as cv
             e["weight_gbs"] = round(wbytes / (ms * 1e-3) / 1e9, 1)
             e["frac_hbm"] = round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
             e["us_per_token"] = round(ms * 1e3 / M, 2)
+            # context: a real TP group's ring all-reduces (2 per layer, bf16) per rank per step
+            e["allreduce_ring_bytes_per_rank"] = int(cv.stack_ring_bytes_per_rank(L, H, 2, T, tokens=M))
         else:
             e["frac_mfma"] = round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
         out["M=%d" % M] = e
@@ -692,64 +767,138 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(args, hl):
+def cpu_baseline(args, hl, dec):
+    """The fp64 oracle on the host cores, timed on bounded samples of the
+    bench's own inputs, and the GPU outputs of those inputs checked against
+    it.  Prefill: a seeded sample of the headline's token rows, sized to take
+    about --cpu-seconds (no step of the block mixes rows, so the time
+    extrapolates linearly to all rows; labelled).  Decode: the whole M = 32
+    step (MLP shard + out-projection shard)."""
     import numpy as np
 
     import oracle
     from megatron_tensor_transformer_colpar_amd import inputs
 
     w = hl["w"]
+    M, H, Fs = w.M, w.H, w.F // w.T
     W1, b1, W2 = hl["W1"].f64, hl["b1"].f64, hl["W2"].f64
-    flops_row = 4.0 * w.H * w.F
+    flops_row = 4.0 * H * Fs
 
     def run(rows):
         Xr = hl["X"].f64[rows]
         t0 = time.perf_counter()
-        zs = [oracle.mlp_shard(Xr, W1, b1, W2, w.T, i)[1] for i in range(w.T)]
-        Zr = oracle.shard_reduce(np.stack(zs))
-        return time.perf_counter() - t0, Zr
+        Yr, Zr = oracle.mlp_shard(Xr, W1, b1, W2, 1, 0)
+        return time.perf_counter() - t0, Yr, Zr
 
     # the oracle threads over rows: probe with two rows per thread so that
     # the rate it measures is the one the full sample will see
-    probe = inputs.row_sample(w.M, max(16, 2 * oracle.max_threads()), seed=1, include_ends=False)
-    dt, _ = run(probe)
-    n = int(min(w.M, max(8, len(probe) * args.cpu_seconds / max(dt, 1e-3))))
-    rows = inputs.row_sample(w.M, n, seed=2)
-    dt, Zr = run(rows)
+    probe = inputs.row_sample(M, max(16, 2 * oracle.max_threads()), seed=1, include_ends=False)
+    dt, _, _ = run(probe)
+    n = int(min(M, max(32, len(probe) * args.cpu_seconds / max(dt, 1e-3))))
+    rows = inputs.row_sample(M, n, seed=2)
+    dt, Yr, Zr = run(rows)
     tflops = len(rows) * flops_row / dt / 1e12
-    got = hl["Z"].double().cpu().numpy()[rows]
-    err = float(np.linalg.norm(got - Zr) / np.linalg.norm(Zr))
-    log("[bench] cpu oracle: %d rows in %.2fs (%.3f GFLOP/s), parity %.2e" % (len(rows), dt, tflops * 1e3, err))
+    rel = lambda got, want: float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    ey = rel(hl["Y"].float().cpu().double().numpy()[rows], Yr)
+    ez = rel(hl["Z"].double().cpu().numpy()[rows], Zr)
+    log("[bench] cpu oracle, prefill: %d rows in %.2fs (%.3f GFLOP/s), parity Y %.2e Z %.2e"
+        % (len(rows), dt, tflops * 1e3, ey, ez))
     cb = {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
-          "sample": "%d of %d token rows of the headline step (all %d shards + reduce, fp64), %.1f s"
-                    % (len(rows), w.M, w.T, dt),
-          "cpu_model": cpu_model()}
-    par = {"rows": len(rows), "rel_fro_Z": err, "tol": 5e-3, "ok": err <= 5e-3}
+          "sample": "%d of %d token rows of the headline step (rank 0's MLP shard, fp64), %.1f s; "
+                    "all %d rows extrapolated: %.1f s" % (len(rows), M, dt, M, dt * M / len(rows)),
+          "extrapolated_s_all_rows": round(dt * M / len(rows), 2), "cpu_model": cpu_model()}
+    par = {"prefill": {"rows": len(rows), "rel_fro_Y": ey, "rel_fro_Z": ez, "tol": 5e-3,
+                       "ok": ey <= 5e-3 and ez <= 5e-3}}
+    if dec is not None:
+        d = dec
+        t0 = time.perf_counter()
+        Yd, Zd = oracle.mlp_shard(d["X"].f64, d["W1"].f64, d["b1"].f64, d["W2"].f64, 1, 0)
+        Od = oracle.rowpar_partial(d["ctx"].f64, d["Wo"].f64, 1, 0)
+        dtd = time.perf_counter() - t0
+        Md, Hd, Fsd, Asd = d["X"].shape[0], d["X"].shape[1], d["W1"].shape[1], d["ctx"].shape[1]
+        by = 2.0 * (2 * Fsd * Hd + Fsd + Asd * Hd) + Md * (Hd * 2 + Asd * 2 + 2 * Hd * 4)
+        cb["decode"] = {"value": round(by / dtd / 1e9, 4), "unit": "GB/s", "seconds": round(dtd, 3),
+                        "sample": "the whole decode step at M=%d (MLP shard + out-projection shard, fp64)" % Md}
+        errs = {}
+        for m, (Y, Z, O) in d["outs"].items():
+            errs["M=%d" % m] = {"Y": rel(Y.float().cpu().double().numpy(), Yd[:m]),
+                                "Z": rel(Z.double().cpu().numpy(), Zd[:m]),
+                                "O": rel(O.double().cpu().numpy(), Od[:m])}
+        par["decode"] = {"rel_fro": errs, "tol": 5e-3,
+                         "ok": all(v <= 5e-3 for e in errs.values() for v in e.values())}
+        log("[bench] cpu oracle, decode: %.2fs, parity %s" % (dtd, errs))
     return cb, par
+
+
+def write_traffic(prof_dir):
+    """profiles/traffic.json from two rocprofv3 --pmc runs of the headline
+    (FETCH_SIZE under <prof_dir>/pmcf, WRITE_SIZE under <prof_dir>/pmcw),
+    each run starting with --copy-calibration: the counters are scaled by
+    what they read for a plain 1 GiB copy (1 GiB read, 1 GiB written)."""
+    import csv
+    import re
+    from collections import defaultdict
+
+    def load(path):
+        d = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            m = re.search(r"(\w+<[^>]*>)\(", name)
+            d[m.group(1) if m else name.split("(")[0]].append(float(r["Counter_Value"]))
+        return d
+
+    F = load(os.path.join(prof_dir, "pmcf", "p_counter_collection.csv"))
+    W = load(os.path.join(prof_dir, "pmcw", "p_counter_collection.csv"))
+    cal = "__amd_rocclr_copyBuffer"
+    sf = round(1048576.0 / (sum(F[cal]) / len(F[cal])), 4)   # counters are KiB per dispatch
+    sw = round(1048576.0 / (sum(W[cal]) / len(W[cal])), 4)
+    M, H, Fs = 8192, 8192, 4096
+    alg = {"gemm_up_gelu": 2 * (M * H + Fs * H + Fs) + 2 * M * Fs, "gemm_rowpar_partial": 2 * (M * Fs + H * Fs) + 4 * M * H}
+    kern = {"gemm_up_gelu": "gemm_bf16_kernel<256, 256, 64, 2, 8, true, 0, 0>",
+            "gemm_rowpar_partial": "gemm_bf16_kernel<256, 256, 64, 2, 8, true, 1, 0>"}
+    try:
+        out = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        out = {}
+    for key, k in kern.items():
+        fr, wr = sum(F[k]) / len(F[k]), sum(W[k]) / len(W[k])
+        out[key + "@prefill"] = {"source": "gemm_bf16.hip", "source_sha": source_sha("gemm_bf16.hip"),
+                                 "kernel": k, "fetch_kib_raw": round(fr), "write_kib_raw": round(wr),
+                                 "fetch_bytes": round(fr * 1024 * sf), "write_bytes": round(wr * 1024 * sw),
+                                 "scale": {"fetch": sf, "write": sw}, "algorithmic_bytes": alg[key],
+                                 "dispatches": len(F[k]), "profile": "profiles/gemm_prefill_rank0_h8192.md"}
+        print(key, json.dumps(out[key + "@prefill"]))
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # 10 warm-up steps (5 ms) leave the first timed steps at a lower clock:
-    # 0.540 against 0.508 ms/step after 100 or more (measured on MI355X)
-    ap.add_argument("--warmup", type=int, default=100)
+    # a minimum: the headline also warms up for at least 200 ms of GPU time
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-sets", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline step only (for profiling)")
-    ap.add_argument("--sections", default="prefill,decode,stack80,variants,attention,backward,context",
+    ap.add_argument("--sections",
+                    default="decode,gpt_block_shard,stack80,variants,attention,backward,context",
                     help="comma-separated extra sections to run after the headline step")
     ap.add_argument("--context-only", action="store_true",
                     help="only the library-vs-hipBLASLt comparison (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
+    ap.add_argument("--write-traffic", metavar="PROF_DIR",
+                    help="write profiles/traffic.json from the FETCH_SIZE/WRITE_SIZE counter runs under PROF_DIR "
+                         "(CPU only) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
 
     import torch
 
@@ -767,14 +916,17 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    hl = headline(args, torch, tp, inputs)
+    hl = prefill_headline(args, torch, tp, inputs)
     kernels = hl["kernels"]
-    dom = max(("gemm_up_gelu", "gemm_rowpar_partial"), key=lambda k: kernels[k]["mean_us"])
+    dom = max(kernels, key=lambda k: kernels[k]["mean_us"])
     ach = kernels[dom]["tflops"]
-    traffic = measured_traffic(dom + "@gpt_block_shard")
+    traffic = measured_traffic(dom + "@prefill")
     roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None if traffic is None else traffic["total_bytes"]}
+            "traffic": None if traffic is None else traffic["total_bytes"],
+            "flops_per_launch": kernels[dom]["flops_per_launch"],
+            "algorithmic_bytes_per_launch": kernels[dom]["algorithmic_bytes_per_launch"],
+            "mean_launch_us": kernels[dom]["mean_us"]}
     if traffic is not None:
         roof["traffic_detail"] = traffic
     value = hl["flops"] / (hl["ms"] * 1e-3) / 1e12
@@ -783,16 +935,25 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(hl["ms"], 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic: seeded N(0,1) activations, N(0,0.02) weights, N(0,0.01) bias (bf16 RNE)",
-           "config": {"workload": "gpt_block_shard: all 4 TP shards + on-device reduce", "M": w.M, "H": w.H,
-                      "F": w.F, "T": w.T, "parallelism": "tp4 emulated on 1 GPU"},
-           "roofline": roof, "kernels": kernels, "ms_per_step_with_kernel_events": round(hl["ms_events"], 4),
-           "per_rank": hl["per_rank"]}
+           "config": {"workload": "prefill, rank 0 of T=8: H=8192, F=32768 (F/T=4096), M=8192 tokens "
+                                  "(4 x 2048); column-parallel GEMM + bias + GeLU, row-parallel fp32 partial",
+                      "M": w.M, "H": w.H, "F": w.F, "T": w.T, "shard": 0, "parallelism": "tp8, rank 0's share"},
+           "frac": round(value / PEAK_BF16_TFLOPS, 4),
+           "roofline": roof, "kernels": kernels, "trials": hl["trials"], "warmup_steps_run": hl["warmup_steps"],
+           "median_tflops": round(hl["flops"] / (hl["trials"]["median_ms"] * 1e-3) / 1e12, 1),
+           "ms_per_step_with_kernel_events": round(hl["ms_events"], 4)}
     sections = set() if args.no_extras else set(x for x in args.sections.split(",") if x)
-    if "prefill" in sections:
-        rec["prefill"] = prefill(args, torch, tp)
+    dec_host = None
     if "decode" in sections:
-        rec["decode"] = decode(args, torch, tp)
+        rec["decode"], dec_host = decode(args, torch, tp, inputs)
+        fr = {k: v["frac"] for k, v in rec["decode"].items() if k.startswith("M=")}
+        rec["decode"]["roofline"] = {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                     "achieved": {k: v["gbs"] for k, v in rec["decode"].items() if k.startswith("M=")},
+                                     "frac": fr}
     torch.cuda.empty_cache()
+    if "gpt_block_shard" in sections:
+        rec["gpt_block_shard"] = gpt_block_shard(args, torch, tp, inputs)
+        torch.cuda.empty_cache()
     if "stack80" in sections:
         rec["stack80"] = stack80(args, torch, tp)
     if "variants" in sections:
@@ -805,7 +966,7 @@ def main():
     if "context" in sections:
         rec["hipblaslt_context"] = hipblaslt_context(args, torch, tp)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, hl)
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, hl, dec_host)
     print(json.dumps(rec), flush=True)
 
 

@@ -8,8 +8,15 @@
  * Sources (page title, then section):
  *  [SLICE]  "Slice the matrix itself" (AI Engineering Visual Guide, Tensor
  *           Parallelism scene): "Column-Parallel & Row-Parallel GEMMs",
- *           "All-Reduce Synchronization", "Mathematical formulation -
- *           row-parallel matrix multiplication summation".
+ *           "All-Reduce Synchronization", "Strict NVLink Domain
+ *           Constraint" (all-reduces on every layer, forward and
+ *           backward), "Mathematical formulation - row-parallel matrix
+ *           multiplication summation".
+ *  [INTERNALS] "Megatron Internals II: Column/Row Parallel Linear and Vocab
+ *           Parallel Embedding" (summary on the Tensor Parallel tag page of
+ *           Duo's Tech Blog): each parallel layer is a contract naming its
+ *           local dimension, the collective that completes it and the
+ *           gradient path that communicates.
  *  [LESSON] "09. Tensor Parallelism in Action: Megatron-LM Matrix Splitting
  *           across NVLink & NVSwitch Networks": section 1 (W1 split by
  *           columns, W2 by rows, one all-reduce, the pipeline diagram),
@@ -334,7 +341,9 @@ size_t tp_attn_workspace_bytes(int64_t Bs, int64_t Sq, int64_t Lk, int32_t nh, i
 
 /*
  * ---- Backward pass of rank i's share (bf16; gradients in fp32) ----
- * [LESSON] forward and backward all-reduces on every layer: the forward's
+ * [SLICE] "Strict NVLink Domain Constraint": all-reduces run on every
+ * layer in the forward and the backward pass; [INTERNALS]: each layer's
+ * contract names the gradient path that communicates.  The forward's
  * All-Reduce-Sum gives every rank the same output gradient dZ, and the
  * column-parallel layer's input gradient is a partial sum that the backward
  * all-reduce completes (on one GPU: tp_shard_reduce over the ranks' dX_i);

@@ -47,9 +47,8 @@ constexpr int kD = 128;           // head dim
 constexpr int kBQ = 128;          // queries per workgroup (4 waves x 32)
 constexpr int kBK = 64;           // keys per tile
 constexpr int kSlots = kBK * kD / 8;  // 16-byte slots per K or V tile (16 KiB)
-constexpr int kDecRows = 8;       // most query rows per key/value head on the decode kernel
-constexpr int kDecMaxChunk = 512; // most keys per decode workgroup
-constexpr int kMaxSplit = 4096;   // most key chunks per sequence on the decode path
+constexpr int kDecMaxChunk = kAttnDecMaxChunk;
+constexpr int kMaxSplit = kAttnMaxSplit;
 
 struct AttnDev {
     const __bf16 *Q, *K, *V;
@@ -528,34 +527,6 @@ hipError_t launch_decode(const AttnDev &d, int chunk, int nsplit, float *ws_o, f
 }
 
 }  // namespace
-
-AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv)
-{
-    AttnPlan p{};
-    const int64_t rows = (int64_t)(nh / nkv) * Sq;
-    p.decode = rows <= kDecRows;
-    if (!p.decode) return p;
-    // enough workgroups to cover the chip four times over (a workgroup
-    // keeps only 16 KiB of its chunk in flight), at most kDecMaxChunk keys
-    // each; measured against two times over: 19.8 vs 22.5 us for 8
-    // sequences of 2048 cached keys, 1 and 32 sequences unchanged
-    const int64_t heads = Bs * nkv;
-    int64_t nsplit = heads > 0 ? (1024 + heads - 1) / heads : 1;
-    nsplit = std::min<int64_t>(nsplit, (Lk + 63) / 64);
-    nsplit = std::max<int64_t>(nsplit, (Lk + kDecMaxChunk - 1) / kDecMaxChunk);
-    int64_t chunk = (Lk + nsplit - 1) / nsplit;
-    chunk = (chunk + 63) / 64 * 64;
-    nsplit = (Lk + chunk - 1) / chunk;
-    if (nsplit > kMaxSplit) {   // caches beyond 2M keys take the matrix-core kernel
-        p.decode = false;
-        return p;
-    }
-    p.nsplit = (int)nsplit;
-    p.chunk = (int)chunk;
-    const int64_t qrows = Bs * Sq * nh;
-    p.ws_bytes = (size_t)(nsplit * qrows * (kD + 2) * 4);
-    return p;
-}
 
 hipError_t launch_attn_bf16(const AttnArgs &x, int num_cu, hipStream_t s)
 {

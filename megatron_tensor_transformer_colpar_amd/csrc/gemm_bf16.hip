@@ -607,27 +607,15 @@ hipError_t launch_gemm_bf16(const GemmArgs &a, Epilogue epi, int num_cu, hipStre
     auto tiles = [&](int bm, int bn) __attribute__((always_inline)) {
         return a.batch * ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
     };
-#ifndef TP_GEMM_IL
-#define TP_GEMM_IL true
-#endif
-#ifndef TP_GEMM_BIG
-#define TP_GEMM_BIG 256, 256, 64, 2, 8
-#endif
-#ifndef TP_GEMM_MID
-#define TP_GEMM_MID 256, 128, 64, 3, 8
-#endif
-#ifndef TP_GEMM_SMALL
-#define TP_GEMM_SMALL 128, 128, 64, 3, 4
-#endif
     if (epi_gated(epi)) {
         // a gated tile writes half its width; the 256x128 shape has a single
         // 32-column accumulator tile per wave and cannot pair gate with up
-        if (tiles(256, 128) >= num_cu) return launch_cfg<TP_GEMM_BIG, TP_GEMM_IL>(a, epi, s);
-        return launch_cfg<TP_GEMM_SMALL, TP_GEMM_IL>(a, epi, s);
+        if (tiles(256, 128) >= num_cu) return launch_cfg<256, 256, 64, 2, 8, true>(a, epi, s);
+        return launch_cfg<128, 128, 64, 3, 4, true>(a, epi, s);
     }
-    if (tiles(256, 256) >= num_cu) return launch_cfg<TP_GEMM_BIG, TP_GEMM_IL>(a, epi, s);
-    if (tiles(256, 128) >= num_cu) return launch_cfg<TP_GEMM_MID, TP_GEMM_IL>(a, epi, s);
-    return launch_cfg<TP_GEMM_SMALL, TP_GEMM_IL>(a, epi, s);
+    if (tiles(256, 256) >= num_cu) return launch_cfg<256, 256, 64, 2, 8, true>(a, epi, s);
+    if (tiles(256, 128) >= num_cu) return launch_cfg<256, 128, 64, 3, 8, true>(a, epi, s);
+    return launch_cfg<128, 128, 64, 3, 4, true>(a, epi, s);
 }
 
 }  // namespace tpk

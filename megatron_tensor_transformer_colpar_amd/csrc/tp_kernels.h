@@ -87,6 +87,10 @@ struct AttnPlan {
     size_t ws_bytes;
 };
 AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv);
+constexpr int kAttnD = 128;             // head dim
+constexpr int kAttnDecRows = 8;         // most query rows per key/value head on the decode kernel
+constexpr int kAttnDecMaxChunk = 512;   // most keys per decode workgroup
+constexpr int kAttnMaxSplit = 4096;     // most key chunks per sequence on the decode path
 hipError_t launch_attn_bf16(const AttnArgs &a, int num_cu, hipStream_t s);
 
 

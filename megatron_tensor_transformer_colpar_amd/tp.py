@@ -30,7 +30,6 @@ if not os.path.exists(LIB_PATH):
         "libtpcolpar.so is not built (%s); build it with "
         "`python -m megatron_tensor_transformer_colpar_amd.build`" % LIB_PATH)
 
-raw = ctypes.CDLL(LIB_PATH)
 
 TP_OK, TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_UNSUPPORTED, TP_ERR_HIP, TP_ERR_ALIAS = range(6)
 STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_UNSUPPORTED",
@@ -42,41 +41,49 @@ TP_RMS_EPS = 1e-6
 TP_MAX_T = 8
 
 _vp, _i64, _i32, _u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
-raw.tp_colpar_gelu.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
-raw.tp_rowpar_partial.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
-raw.tp_shard_reduce.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _i64, _i64, _u32, _vp]
-raw.tp_mlp_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
 _pp = ctypes.POINTER(_vp)
-raw.tp_colpar_gelu_group.argtypes = [_vp, _vp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
-raw.tp_rowpar_partial_group.argtypes = [_pp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
-raw.tp_mlp_group_fwd.argtypes = [_vp, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
-raw.tp_layer_fwd.argtypes = [_vp, _vp, _pp, _vp, _i64, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _vp]
-raw.tp_colpar_act.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
-raw.tp_colpar_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
-raw.tp_colpar_linear.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
-raw.tp_qkv_colpar.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
-                              _i32, _i32, _i32, _vp]
-raw.tp_attn_core.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i32,
-                             _vp, ctypes.c_size_t, _vp]
-raw.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i32]
-raw.tp_attn_workspace_bytes.restype = ctypes.c_size_t
-raw.tp_colpar_act_train.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
-raw.tp_rowpar_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _u32, _vp]
-raw.tp_colpar_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _u32, _vp]
-raw.tp_mlp_shard_bwd.argtypes = [_vp] * 11 + [_i64, _i64, _i64, _i32, _i32, _i32, _u32, _vp]
-raw.tp_mlp_group_fwd_train.argtypes = [_vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
-raw.tp_mlp_group_bwd.argtypes = [_vp, _vp, _vp, _pp, _pp, _vp, _pp, _pp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
-                                 _u32, _vp]
-for _f in (raw.tp_colpar_gelu, raw.tp_rowpar_partial, raw.tp_shard_reduce, raw.tp_mlp_shard_fwd,
-           raw.tp_colpar_gelu_group, raw.tp_rowpar_partial_group, raw.tp_mlp_group_fwd, raw.tp_layer_fwd,
-           raw.tp_colpar_act, raw.tp_colpar_gated, raw.tp_colpar_linear, raw.tp_qkv_colpar, raw.tp_attn_core,
-           raw.tp_colpar_act_train, raw.tp_rowpar_bwd, raw.tp_colpar_bwd, raw.tp_mlp_shard_bwd,
-           raw.tp_mlp_group_fwd_train, raw.tp_mlp_group_bwd):
-    _f.restype = ctypes.c_int
-raw.tp_last_error.argtypes = []
-raw.tp_last_error.restype = ctypes.c_char_p
-raw.tp_version.argtypes = []
-raw.tp_version.restype = ctypes.c_char_p
+
+
+def _bind(lib):
+    """Declare the C signatures of include/tp_colpar.h on a loaded build of the library."""
+    lib.tp_colpar_gelu.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+    lib.tp_rowpar_partial.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+    lib.tp_shard_reduce.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _i64, _i64, _u32, _vp]
+    lib.tp_mlp_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+    lib.tp_colpar_gelu_group.argtypes = [_vp, _vp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
+    lib.tp_rowpar_partial_group.argtypes = [_pp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
+    lib.tp_mlp_group_fwd.argtypes = [_vp, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
+    lib.tp_layer_fwd.argtypes = [_vp, _vp, _pp, _vp, _i64, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _vp]
+    lib.tp_colpar_act.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
+    lib.tp_colpar_gated.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _vp]
+    lib.tp_colpar_linear.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+    lib.tp_qkv_colpar.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                  _i32, _i32, _i32, _vp]
+    lib.tp_attn_core.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _i64, _i64, _i64, _i32,
+                                 _vp, ctypes.c_size_t, _vp]
+    lib.tp_attn_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i32]
+    lib.tp_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.tp_colpar_act_train.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+    lib.tp_rowpar_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _u32, _vp]
+    lib.tp_colpar_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _u32, _vp]
+    lib.tp_mlp_shard_bwd.argtypes = [_vp] * 11 + [_i64, _i64, _i64, _i32, _i32, _i32, _u32, _vp]
+    lib.tp_mlp_group_fwd_train.argtypes = [_vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
+    lib.tp_mlp_group_bwd.argtypes = [_vp, _vp, _vp, _pp, _pp, _vp, _pp, _pp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
+                                     _u32, _vp]
+    for _f in (lib.tp_colpar_gelu, lib.tp_rowpar_partial, lib.tp_shard_reduce, lib.tp_mlp_shard_fwd,
+               lib.tp_colpar_gelu_group, lib.tp_rowpar_partial_group, lib.tp_mlp_group_fwd, lib.tp_layer_fwd,
+               lib.tp_colpar_act, lib.tp_colpar_gated, lib.tp_colpar_linear, lib.tp_qkv_colpar, lib.tp_attn_core,
+               lib.tp_colpar_act_train, lib.tp_rowpar_bwd, lib.tp_colpar_bwd, lib.tp_mlp_shard_bwd,
+               lib.tp_mlp_group_fwd_train, lib.tp_mlp_group_bwd):
+        _f.restype = ctypes.c_int
+    lib.tp_last_error.argtypes = []
+    lib.tp_last_error.restype = ctypes.c_char_p
+    lib.tp_version.argtypes = []
+    lib.tp_version.restype = ctypes.c_char_p
+    return lib
+
+
+raw = _bind(ctypes.CDLL(LIB_PATH))
 
 EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_shard_fwd",
            "tp_colpar_gelu_group", "tp_rowpar_partial_group", "tp_mlp_group_fwd", "tp_layer_fwd",

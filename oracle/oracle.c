@@ -180,8 +180,9 @@ int orc_colpar_gated(int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, int3
     return ORC_OK;
 }
 
-/* Row-parallel partial product of shard i ([SLICE] Z = sum_i Y_i V_i and
- * "row-parallel outputs are local partial sums"; [LESSON] W2 split into the
+/* Row-parallel partial product of shard i ([SLICE] "Mathematical
+ * formulation - row-parallel matrix multiplication summation": Z = sum_i
+ * Y_i V_i, each rank holding only its own term; [LESSON] W2 split into the
  * row blocks [W2,1 ; W2,2]; [GUIDE] row-parallel shards W along the input
  * dimension):
  *   Z_i[m][n] = sum_{c=0}^{F/T-1} Y_i[m][c] * W2[o+c][n],   o = i*F/T.
@@ -285,8 +286,10 @@ int orc_act_grad(int32_t act, int64_t n, const double *x, double *y)
 /* Backward pass of rank i's MLP share, given dZ [M][H], the gradient of the
  * loss at the block's output Z = sum_j Z_j.  The forward all-reduce hands
  * every rank the same dZ, and the column-parallel input's gradient needs an
- * all-reduce in the backward pass ([LESSON] forward and backward all-reduces
- * on every layer; the column- and row-parallel layers' gradient contracts).
+ * all-reduce in the backward pass ("Slice the matrix itself", "Strict NVLink
+ * Domain Constraint": all-reduces on every layer, forward and backward; the
+ * "Megatron Internals II" summary on the Tensor Parallel tag page: each
+ * parallel layer's contract names the gradient path that communicates).
  * With U_i = X W1[:, C_i] + b1[C_i], Y_i = g(U_i), Z_i = Y_i W2[C_i, :]:
  *   dY_i        = dZ W2[C_i, :]^T               [M][Fs]
  *   dU_i        = dY_i * g'(U_i)   (elementwise)

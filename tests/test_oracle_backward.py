@@ -5,9 +5,10 @@ closed-form identities, exact integer products, and the shard algebra (the
 ranks' dX partials sum to the unsharded dX; the ranks' weight-gradient
 blocks are the unsharded gradient's blocks).
 
-Sources: "09. Tensor Parallelism in Action" (forward and backward all-reduces
-on every layer; the gradient contracts of the column- and row-parallel
-layers); Hendrycks & Gimpel, arXiv:1606.08415 (GeLU and its exact form).
+Sources: "Slice the matrix itself", "Strict NVLink Domain Constraint"
+(all-reduces on every layer, forward and backward); the "Megatron Internals
+II" summary on the Tensor Parallel tag page (each parallel layer's contract
+names the gradient path that communicates); Hendrycks & Gimpel, arXiv:1606.08415 (GeLU and its exact form).
 Everything runs on the CPU.
 """
 import math

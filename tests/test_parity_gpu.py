@@ -87,24 +87,51 @@ def test_bf16_smallest_gemm_m():
     check_all_shards(w, M=33, T=2, use_fused=False)
 
 
+def tile_row_sample(M, extra, seed=0):
+    """First and last row of every 256-row tile row, plus `extra` seeded rows:
+    a wrong tile row anywhere shows in the sample."""
+    ends = {r for t in range(0, M, 256) for r in (t, min(M, t + 256) - 1)}
+    return np.array(sorted(ends | set(inputs.row_sample(M, extra, seed=seed).tolist())), dtype=np.int64)
+
+
+def per_block(got, want, rows, what):
+    """rel-Frobenius of each 256-row block of the sample (each <= the bf16 bar)."""
+    worst = 0.0
+    for b in np.unique(rows // 256):
+        sel = rows // 256 == b
+        e = rel_fro(got[sel], want[sel])
+        assert e <= TOL["bf16"], (what, int(b), e)
+        worst = max(worst, e)
+    return worst
+
+
 def test_gpt_block_shard_full_size_sampled_rows():
-    # H=4096, F=16384, T=4, M=2048: all 4 shards and the reduce, as benchmarked
+    # H=4096, F=16384, T=4, M=2048: all 4 shards and the reduce, as benchmarked;
+    # both ends of every 256-row tile row plus 16 seeded rows
     w = inputs.WORKLOADS["gpt_block_shard"]
-    check_all_shards(w, M=w.M, T=w.T, rows=inputs.row_sample(w.M, 12))
+    check_all_shards(w, M=w.M, T=w.T, rows=tile_row_sample(w.M, 16))
 
 
-def test_prefill_full_size_sampled_rows():
-    # H=8192, F=32768, T=8: rank 0's own weight blocks (F := F/T, T := 1), M=8192
+def test_prefill_full_size_every_tile_row():
+    # H=8192, F=32768, T=8: rank 0's own weight blocks (F := F/T, T := 1),
+    # M=8192, the launch configuration the bench times: the first and last row
+    # of each of the 32 tile rows plus 64 seeded rows, error per 256-row block
     w = inputs.WORKLOADS["prefill"]
     X, W1, b1, W2 = inputs.mlp_inputs(w, shard_only=0)
     dev = DeviceMLP(X, W1, b1, W2)
-    Y, Z = dev.shard(1, 0)
+    Y, Z = dev.shard(1, 0, use_fused=False)
     torch.cuda.synchronize()
-    rows = inputs.row_sample(w.M, 8)
+    rows = tile_row_sample(w.M, 64)
     Yr, Zr = oracle.mlp_shard(X.f64[rows], W1.f64, b1.f64, W2.f64, 1, 0)
-    ey, ez = rel_fro(to_f64(Y)[rows], Yr), rel_fro(to_f64(Z)[rows], Zr)
-    print("  Y_0 %.2e  Z_0 %.2e" % (ey, ez))
+    Yg, Zg = to_f64(Y)[rows], to_f64(Z)[rows]
+    ey, ez = rel_fro(Yg, Yr), rel_fro(Zg, Zr)
+    by, bz = per_block(Yg, Yr, rows, "Y"), per_block(Zg, Zr, rows, "Z")
+    print("  %d rows: Y_0 %.2e  Z_0 %.2e  (worst 256-row block: Y %.2e  Z %.2e)" % (len(rows), ey, ez, by, bz))
     assert ey <= TOL["bf16"] and ez <= TOL["bf16"]
+    # the fused entry point computes the same bits
+    Y2, Z2 = dev.shard(1, 0, use_fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2) and torch.equal(Z, Z2)
 
 
 @pytest.mark.parametrize("M,H,Fs", [(4196, 4096, 4096), (4096, 4160, 4160)])
