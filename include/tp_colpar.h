@@ -206,6 +206,32 @@ tp_status tp_mlp_shard_fwd(const void *X, const void *W1t, const void *b1, const
                            int32_t T, int32_t i, tp_dtype dt, hipStream_t stream);
 
 /*
+ * tp_mlp_shard_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same two launches, with Y_i staged in the library's own
+ * device buffer instead of a caller workspace.  The caller still passes
+ * every input and the output Z_i [M][H] fp32; the call allocates nothing
+ * (no hipMalloc, no allocating library routine).
+ *   Limit: M * F/T * (2 for TP_BF16, 4 for TP_F32) <= TP_NOALLOC_SCRATCH_BYTES
+ *          (16 MiB: every decode shape; prefill up to 2048 tokens at
+ *          F/T = 4096 in bf16); larger calls return TP_ERR_UNSUPPORTED
+ *          before any HIP call.
+ *   The buffer is one file-scope device array per GPU, held until the
+ *   process ends and shared by every call on that GPU: calls on one GPU
+ *   whose executions overlap (two streams, two threads) race on it and must
+ *   be ordered by the caller.  Y_i is written in full before it is read, so
+ *   nothing needs clearing between calls.
+ * Validation as tp_mlp_shard_fwd (without Y_ws): TP_ERR_NULL for a NULL X,
+ * W1t, W2t or Z_i; the shape and alignment codes of tp_colpar_gelu; Z_i
+ * overlapping an input is TP_ERR_ALIAS.  The first call on a device looks up
+ * the buffer's address (TP_ERR_HIP if that fails).
+ */
+#define TP_NOALLOC_SCRATCH_BYTES 16777216
+tp_status tp_mlp_shard_fwd_noalloc(const void *X, const void *W1t, const void *b1, const void *W2t,
+                                   float *Z_i, int64_t M, int64_t H, int64_t F, int32_t T,
+                                   int32_t i, tp_dtype dt, hipStream_t stream);
+
+/*
  * All T ranks' shares at once, for emulating the whole TP group on one GPU
  * ([LESSON] section 1: every rank runs the same column- then row-parallel
  * pair on its own blocks; [SLICE] summation formula: the T partials are what

@@ -24,7 +24,7 @@ CXX = os.environ.get("CXX", "g++")
 ROCM_INCLUDE = "/opt/rocm/include"
 ARCH = "gfx950"
 
-SOURCES = ["gemm_bf16.hip", "gemv_bf16.hip", "gemm_f32.hip", "attn_bf16.hip", "reduce.hip", "plan.cpp", "abi.cpp"]
+SOURCES = ["gemm_bf16.hip", "gemv_bf16.hip", "gemm_f32.hip", "attn_bf16.hip", "reduce.hip", "scratch.hip", "plan.cpp", "abi.cpp"]
 COMMON = ["-O3", "-std=c++20", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 HIP_ONLY = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -449,6 +449,36 @@ tp_status tp_mlp_shard_fwd(const void *X, const void *W1t, const void *b1, const
     return run_rowpar(&y_in, W2t, &Z_i, 1, i, M, H, F, T, dt, stream);
 }
 
+tp_status tp_mlp_shard_fwd_noalloc(const void *X, const void *W1t, const void *b1, const void *W2t, float *Z_i,
+                                   int64_t M, int64_t H, int64_t F, int32_t T, int32_t i, tp_dtype dt,
+                                   hipStream_t stream)
+{
+    static_assert(TP_NOALLOC_SCRATCH_BYTES == tpk::kScratchBytes, "header and library disagree on the limit");
+    const char *fn = "tp_mlp_shard_fwd_noalloc";
+    tp_status st = check_shard(fn, M, H, F, T, i, dt);
+    if (st != TP_OK) return st;
+    if (!X || !W1t || !W2t || !Z_i) return fail(TP_ERR_NULL, "%s: X, W1t, W2t and Z_i must be non-NULL", fn);
+    if ((st = check_dims64(fn, H, F, T)) != TP_OK) return st;
+    if (!aligned16(X) || !aligned16(W1t) || !aligned16(W2t) || !aligned16(Z_i) || (b1 && !aligned16(b1)))
+        return fail(TP_ERR_UNSUPPORTED, "%s: X, W1t, b1, W2t and Z_i must be 16-byte aligned", fn);
+    const int es = element_size(dt);
+    const int64_t need = M * (F / T) * es;
+    if (need > TP_NOALLOC_SCRATCH_BYTES)
+        return fail(TP_ERR_UNSUPPORTED, "%s: staging Y_i needs %lld bytes, above the %lld-byte limit", fn,
+                    (long long)need, (long long)TP_NOALLOC_SCRATCH_BYTES);
+    const Range z = span(Z_i, M * H * 4);
+    if (M > 0 && (overlap(z, span(X, M * H * es)) || overlap(z, span(W1t, F * H * es)) ||
+                  (b1 && overlap(z, span(b1, F * es))) || overlap(z, span(W2t, H * F * es))))
+        return fail(TP_ERR_ALIAS, "%s: Z_i overlaps an input", fn);
+    if (M == 0) return ok();
+    void *Y = nullptr;
+    const hipError_t e = tpk::scratch_base(&Y);
+    if (e != hipSuccess) return hip_fail(e, "tp_mlp_shard_fwd_noalloc: staging buffer lookup");
+    if ((st = run_colpar(X, W1t, b1, &Y, 1, i, M, H, F, T, dt, stream)) != TP_OK) return st;
+    const void *y_in = Y;
+    return run_rowpar(&y_in, W2t, &Z_i, 1, i, M, H, F, T, dt, stream);
+}
+
 tp_status tp_colpar_gelu_group(const void *X, const void *W1t, const void *b1, void *const *Y_ws, int64_t M,
                                int64_t H, int64_t F, int32_t T, tp_dtype dt, hipStream_t stream)
 {

@@ -106,4 +106,10 @@ hipError_t launch_shard_reduce(const float *const *partials, int T, const float 
                                float *out, void *out_bf16, int64_t M, int64_t H, bool rms,
                                float eps, hipStream_t s);
 
+// Staging area of tp_mlp_shard_fwd_noalloc: a file-scope device array of
+// kScratchBytes per GPU (scratch.hip).  scratch_base gives this device's
+// copy's address (looked up once per device, the device current).
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+hipError_t scratch_base(void **out);
+
 }  // namespace tpk

@@ -39,6 +39,7 @@ TP_GELU_TANH, TP_GELU_ERF = 0, 1
 TP_REDUCE_RMS_BF16 = 1
 TP_RMS_EPS = 1e-6
 TP_MAX_T = 8
+TP_NOALLOC_SCRATCH_BYTES = 16777216
 
 _vp, _i64, _i32, _u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
 _pp = ctypes.POINTER(_vp)
@@ -50,6 +51,7 @@ def _bind(lib):
     lib.tp_rowpar_partial.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
     lib.tp_shard_reduce.argtypes = [ctypes.POINTER(_vp), _i32, _vp, _vp, _vp, _i64, _i64, _u32, _vp]
     lib.tp_mlp_shard_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
+    lib.tp_mlp_shard_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _i32, _vp]
     lib.tp_colpar_gelu_group.argtypes = [_vp, _vp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
     lib.tp_rowpar_partial_group.argtypes = [_pp, _vp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
     lib.tp_mlp_group_fwd.argtypes = [_vp, _vp, _vp, _vp, _pp, _pp, _i64, _i64, _i64, _i32, _i32, _vp]
@@ -71,6 +73,7 @@ def _bind(lib):
     lib.tp_mlp_group_bwd.argtypes = [_vp, _vp, _vp, _pp, _pp, _vp, _pp, _pp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32,
                                      _u32, _vp]
     for _f in (lib.tp_colpar_gelu, lib.tp_rowpar_partial, lib.tp_shard_reduce, lib.tp_mlp_shard_fwd,
+               lib.tp_mlp_shard_fwd_noalloc,
                lib.tp_colpar_gelu_group, lib.tp_rowpar_partial_group, lib.tp_mlp_group_fwd, lib.tp_layer_fwd,
                lib.tp_colpar_act, lib.tp_colpar_gated, lib.tp_colpar_linear, lib.tp_qkv_colpar, lib.tp_attn_core,
                lib.tp_colpar_act_train, lib.tp_rowpar_bwd, lib.tp_colpar_bwd, lib.tp_mlp_shard_bwd,
@@ -85,7 +88,7 @@ def _bind(lib):
 
 raw = _bind(ctypes.CDLL(LIB_PATH))
 
-EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_shard_fwd",
+EXPORTS = ("tp_colpar_gelu", "tp_rowpar_partial", "tp_shard_reduce", "tp_mlp_shard_fwd", "tp_mlp_shard_fwd_noalloc",
            "tp_colpar_gelu_group", "tp_rowpar_partial_group", "tp_mlp_group_fwd", "tp_layer_fwd",
            "tp_colpar_act", "tp_colpar_gated", "tp_colpar_linear", "tp_qkv_colpar", "tp_attn_core",
            "tp_attn_workspace_bytes", "tp_colpar_act_train", "tp_rowpar_bwd", "tp_colpar_bwd", "tp_mlp_shard_bwd",
@@ -157,6 +160,11 @@ def tp_mlp_shard_fwd(X, W1t, b1, W2t, Y_ws, Z_i, M, H, F, T, i, dt=TP_BF16, stre
 
 def _arr(xs):
     return xs if isinstance(xs, ctypes.Array) else partial_array(xs)
+
+
+def tp_mlp_shard_fwd_noalloc(X, W1t, b1, W2t, Z_i, M, H, F, T, i, dt=TP_BF16, stream=None):
+    _check(raw.tp_mlp_shard_fwd_noalloc(_ptr(X), _ptr(W1t), _ptr(b1), _ptr(W2t), _ptr(Z_i), M, H, F, T, i, dt,
+                                        _stream(stream)))
 
 
 def tp_colpar_gelu_group(X, W1t, b1, Y_ws, M, H, F, T, dt=TP_BF16, stream=None):

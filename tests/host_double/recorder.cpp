@@ -89,6 +89,13 @@ hipError_t launch_shard_reduce(const float *const *partials, int T, const float 
     return hipSuccess;
 }
 
+// the staging buffer of tp_mlp_shard_fwd_noalloc: a fake, 256-byte aligned address
+hipError_t scratch_base(void **out)
+{
+    *out = reinterpret_cast<void *>(uintptr_t(0xABC) << 32);
+    return hipSuccess;
+}
+
 }  // namespace tpk
 
 // The HIP runtime calls of abi.cpp: one device with 256 compute units.

@@ -80,3 +80,17 @@ def test_decode_path_below_33_tokens(M, kind):
     assert tp.raw.tp_colpar_gelu(P[0], P[1], P[2], P[3], M, 8192, 32768, 8, 0, 0, None) == 0
     assert tp.raw.tp_colpar_gelu(P[0], P[1], P[2], P[3], M, 256, 1024, 2, 1, 1, None) == 0
     assert [e[0] for e in plugin.log()] == [kind, GEMM_F32]
+
+
+def test_noalloc_shard_stages_in_the_library_buffer():
+    # the no-allocation variant runs the same two launches as tp_mlp_shard_fwd,
+    # with Y_i in the library's staging buffer; at the limit it still launches
+    from megatron_tensor_transformer_colpar_amd import tp
+
+    plugin.recorder.rec_reset()
+    assert tp.raw.tp_mlp_shard_fwd_noalloc(P[0], P[1], P[2], P[3], P[5], 8, 8192, 32768, 8, 3, 0, None) == 0
+    assert tp.raw.tp_mlp_shard_fwd_noalloc(P[0], P[1], P[2], P[3], P[5], 2048, 4096, 4096, 1, 0, 0, None) == 0
+    log = plugin.log()
+    assert [e[0] for e in log] == [GEMV, GEMV, GEMM, GEMM]
+    assert [e[1] for e in log] == [EPI_BIAS_GELU, EPI_STORE_F32] * 2
+    assert plugin.recorder.rec_violations() == 0

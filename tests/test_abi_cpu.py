@@ -112,6 +112,38 @@ def test_mlp_shard_rejects(kw, status):
     assert "tp_mlp_shard_fwd" in tp.last_error()
 
 
+def mlp_noalloc(X=P[0], W1=P[1], b=P[2], W2=P[4], Z=P[5], M=4, H=64, F=256, T=4, i=0, dt=BF16):
+    return tp.raw.tp_mlp_shard_fwd_noalloc(X, W1, b, W2, Z, M, H, F, T, i, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), tp.TP_ERR_NULL),
+    (dict(W1=None), tp.TP_ERR_NULL),
+    (dict(W2=None), tp.TP_ERR_NULL),
+    (dict(Z=None), tp.TP_ERR_NULL),
+    (dict(T=3), tp.TP_ERR_SHAPE),
+    (dict(i=4), tp.TP_ERR_SHAPE),
+    (dict(H=96), tp.TP_ERR_UNSUPPORTED),
+    (dict(Z=P[5] + 4), tp.TP_ERR_UNSUPPORTED),
+    # the staging limit: 4096 x 4096 bf16 is 32 MiB, 2 x the 16 MiB buffer
+    (dict(M=4096, H=64, F=4096, T=1), tp.TP_ERR_UNSUPPORTED),
+    (dict(M=2049, H=64, F=16384, T=4), tp.TP_ERR_UNSUPPORTED),
+    (dict(M=1025, H=64, F=4096, T=1, dt=F32), tp.TP_ERR_UNSUPPORTED),
+    (dict(Z=P[0]), tp.TP_ERR_ALIAS),        # Z over X
+    (dict(Z=P[4] + 256), tp.TP_ERR_ALIAS),  # Z over W2t
+])
+def test_mlp_noalloc_rejects(kw, status):
+    assert mlp_noalloc(**kw) == status
+    assert "tp_mlp_shard_fwd_noalloc" in tp.last_error()
+    if kw.get("M", 0) >= 1024:
+        assert "limit" in tp.last_error()
+
+
+def test_mlp_noalloc_limit_and_empty_call():
+    assert tp.TP_NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert mlp_noalloc(M=0) == tp.TP_OK
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(T=0), tp.TP_ERR_SHAPE),
     (dict(T=9, parts=[P[6]] * 9), tp.TP_ERR_SHAPE),
