@@ -427,7 +427,7 @@ def attention(args, torch, tp):
         Q = torch.empty(Bs, As, dtype=torch.bfloat16, device="cuda")
         ctx = torch.empty(Bs, As, dtype=torch.bfloat16, device="cuda")
         nws = tp.tp_attn_workspace_bytes(Bs, 1, L, nh, nh)
-        ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(nws, dtype=torch.uint8, device="cuda")   # arrival counters start at zero
 
         def qkv(k):
             wq, wk, wv = wsets[k % R]
@@ -854,8 +854,16 @@ def write_traffic(prof_dir):
     sw = round(1048576.0 / (sum(W[cal]) / len(W[cal])), 4)
     M, H, Fs = 8192, 8192, 4096
     alg = {"gemm_up_gelu": 2 * (M * H + Fs * H + Fs) + 2 * M * Fs, "gemm_rowpar_partial": 2 * (M * Fs + H * Fs) + 4 * M * H}
-    kern = {"gemm_up_gelu": "gemm_bf16_kernel<256, 256, 64, 2, 8, true, 0, 0>",
-            "gemm_rowpar_partial": "gemm_bf16_kernel<256, 256, 64, 2, 8, true, 1, 0>"}
+    # the headline's two launches: 256x256 tiles, 8 waves, epilogue 0 (bias +
+    # GeLU) and 1 (fp32 partial), K-contiguous operands
+    def pick(epi):
+        for name in F:
+            args = [a.strip() for a in name[name.find("<") + 1:name.rfind(">")].split(",")]
+            if name.startswith("gemm_bf16_kernel<") and args[:5] == ["256", "256", "64", "2", "8"] and \
+                    args[6:8] == [str(epi), "0"]:
+                return name
+        raise KeyError("no headline kernel with epilogue %d in the counter runs" % epi)
+    kern = {"gemm_up_gelu": pick(0), "gemm_rowpar_partial": pick(1)}
     try:
         out = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):

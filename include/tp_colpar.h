@@ -342,11 +342,18 @@ tp_status tp_qkv_colpar(const void *X, const void *Wq_t, const void *Wk_t, const
  * position kv_len[b] - Sq + s.  causal != 0: it sees keys 0 .. its position;
  * causal == 0: keys 0 .. kv_len[b]-1.  Query head h reads key/value head
  * h / (nh / nkv).  A query row that sees no key is written as zeros.
- * When G*Sq <= 8 (G = nh/nkv) the keys are split over many workgroups and
- * merged in a second launch: that path needs `workspace`, a device buffer of
- * at least tp_attn_workspace_bytes(Bs, Sq, Lk, nh, nkv) bytes (the
- * partials; it may be reused once the call's work has run).  Otherwise the
- * workspace is not touched and may be NULL.
+ * When G*Sq <= 8 (G = nh/nkv) and Bs*nkv <= 4096 the keys are split over
+ * many workgroups of one launch, and the last workgroup of each (sequence,
+ * key/value head) to finish merges the chunks (in chunk order: the result
+ * does not depend on which one finishes last).  That path needs
+ * `workspace`, a device buffer of at least
+ * tp_attn_workspace_bytes(Bs, Sq, Lk, nh, nkv) bytes: 4096 arrival counters
+ * (16 KiB) at its start, then the chunks' partials.  The counters must be
+ * zero when the workspace is first used (allocate it zero-filled); every
+ * call returns them to zero, so the buffer can serve any later call, of any
+ * shape, whose work is ordered after this one's (calls that overlap in time
+ * must not share a workspace).  Otherwise the workspace is not touched and
+ * may be NULL.
  * Validation: Bs, Sq >= 0, Lk >= 1, nh, nkv >= 1, nh % nkv == 0, causal
  * needs Sq <= Lk, ldq and ldo >= nh*128, ldkv >= nkv*128 (TP_ERR_SHAPE);
  * Q, K, V, ctx non-NULL, workspace non-NULL when needed (TP_ERR_NULL);
@@ -361,8 +368,8 @@ tp_status tp_attn_core(const void *Q, const void *K, const void *V, void *ctx, c
                        int64_t ldq, int64_t ldkv, int64_t ldo, int32_t causal, void *workspace,
                        size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes tp_attn_core needs for these sizes (0: none).  Depends on
- * the sizes only, not on the device. */
+/* Workspace bytes tp_attn_core needs for these sizes (0: none), counters
+ * included.  Depends on the sizes only, not on the device. */
 size_t tp_attn_workspace_bytes(int64_t Bs, int64_t Sq, int64_t Lk, int32_t nh, int32_t nkv);
 
 /*

@@ -25,8 +25,10 @@
 // * attn_decode_kernel (a few rows: decode), memory-bound: the keys of a
 //   sequence are split into chunks spread over many workgroups; each streams
 //   its chunk of K and then of V once, 16 lanes per 256-byte row, and writes
-//   an unnormalised partial (max, sum, weighted values).  attn_combine_kernel
-//   merges the chunks of every query row.
+//   an unnormalised partial (max, sum, weighted values).  Each workgroup then
+//   counts its arrival for its (sequence, key/value head); the last to
+//   arrive merges the chunks of those query rows in chunk order and resets
+//   the counter, so the decode step is one launch and no workgroup waits.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -321,6 +323,18 @@ __device__ __forceinline__ void bf16x8_to_f32(u32x4 w, float *f)
     }
 }
 
+// Device-coherent accesses to the split-key partials: relaxed atomics at
+// agent scope, which bypass the per-XCD L2s, so a workgroup on another XCD
+// reads what was written.
+__device__ __forceinline__ void publish(float *p, float x)
+{
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch(const float *p)
+{
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Workgroup (b, g, c): keys [c*chunk, (c+1)*chunk) of sequence b against the
 // NR = G*Sq query rows that read key/value head g (row r = gq*Sq + s is query
 // s of head g*G + gq).  Lane layout over a K or V row: lanes 16k .. 16k+15
@@ -328,10 +342,15 @@ __device__ __forceinline__ void bf16x8_to_f32(u32x4 w, float *f)
 // Partial of row r, chunk c: max m, sum l = sum_t 2^(x_t - m), o[d] =
 // sum_t 2^(x_t - m) v_t[d], x_t the scaled score in log2 units.
 template <int NR>
-__global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, int nsplit, float *ws_o, float *ws_ml)
+__global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, int nsplit, float *ws_o, float *ws_ml,
+                                                          unsigned *arrivals)
 {
-    __shared__ float p_lds[kDecMaxChunk][NR];   // scores, then weights: [key][row]
-    __shared__ float red[4][NR][kD];            // per-wave partial outputs
+    // scores then weights [key][row], then per-wave partial outputs; the
+    // merge reuses the space for the chunk weights of two rows at a time
+    constexpr int kPart = kDecMaxChunk * NR + 4 * NR * kD;
+    __shared__ float smem[kPart > 2 * kMaxSplit ? kPart : 2 * kMaxSplit];
+    float(*p_lds)[NR] = reinterpret_cast<float(*)[NR]>(smem);
+    float(*red)[NR][kD] = reinterpret_cast<float(*)[NR][kD]>(smem + kDecMaxChunk * NR);
     __shared__ float ml[NR][2];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -457,72 +476,95 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, 
         const float x = red[0][r][d] + red[1][r][d] + red[2][r][d] + red[3][r][d];
         const int gq = r / a.Sq, s = r % a.Sq;
         const int64_t row = (((int64_t)c * a.Bs + b) * a.Sq + s) * a.nh + g * a.G + gq;
-        ws_o[row * kD + d] = x;
+        publish(ws_o + row * kD + d, x);
         if (d == 0) {
-            ws_ml[2 * row] = ml[r][0];
-            ws_ml[2 * row + 1] = ml[r][1];
+            publish(ws_ml + 2 * row, ml[r][0]);
+            publish(ws_ml + 2 * row + 1, ml[r][1]);
         }
     }
-}
 
-// One workgroup per (b, s, head) query row, one lane per dim.  The chunks'
-// maxima and sums are read in parallel (lane c takes chunk c, c + 128, ...)
-// and reduced through LDS; the weighted rows are then summed with eight
-// loads in flight per lane.
-__global__ void __launch_bounds__(kD) attn_combine_kernel(AttnDev a, int nsplit, const float *ws_o,
-                                                          const float *ws_ml)
-{
-    __shared__ float red[kD / 64];
-    __shared__ float wts[kMaxSplit];
-    const int t = threadIdx.x;
-    const int64_t qrow = blockIdx.x;   // (b * Sq + s) * nh + hq
+    // Count the arrival; the last of the nsplit workgroups of (b, g) to
+    // arrive merges every chunk of its rows and returns the counter to zero
+    // for the next call.  No workgroup waits on another.  The partials are
+    // written and read with device-coherent accesses (they bypass the
+    // per-XCD L2s), and every store has completed before the arrival is
+    // counted, so the merging workgroup reads all of them; no L2 write-back
+    // or invalidation is needed (an agent-scope fence here, which does both,
+    // took the M = 8 decode step from 20 to 159 us).  The merge sums the
+    // chunks in chunk order, so the result does not depend on which
+    // workgroup arrives last.
+    __shared__ int merge;
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's partial stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0)
+        merge = __hip_atomic_fetch_add(arrivals + bg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (unsigned)(nsplit - 1);
+    __syncthreads();
+    if (!merge) return;
+
+    // merge, two query rows at a time, one half-workgroup (128 lanes, one
+    // per dim) per row: weight of chunk c = 2^(m_c - M) (chunks without a
+    // visible key weigh 0), ctx = sum_c w_c o_c / sum_c w_c l_c
+    __shared__ float hred[2][2];
+    const int half = threadIdx.x >> 7, t = threadIdx.x & 127, hw = (threadIdx.x >> 6) & 1;
+    float *const wts = smem + half * kMaxSplit;
     const int64_t stride = (int64_t)a.Bs * a.Sq * a.nh;
-    float M = -INFINITY;
-    for (int c = t; c < nsplit; c += kD) {
-        const float2 ml = *reinterpret_cast<const float2 *>(ws_ml + 2 * (c * stride + qrow));
-        if (ml.y > 0.0f) M = fmaxf(M, ml.x);
+    for (int r0 = 0; r0 < rows; r0 += 2) {
+        const int r = r0 + half;
+        const bool live = r < rows;
+        const int rr = live ? r : 0;
+        const int gq = rr / a.Sq, sq = rr % a.Sq;
+        const int64_t qrow = ((int64_t)b * a.Sq + sq) * a.nh + g * a.G + gq;
+        float M = -INFINITY;
+        for (int cc2 = t; cc2 < nsplit; cc2 += kD) {
+            const float m2x = fetch(ws_ml + 2 * (cc2 * stride + qrow)), m2y = fetch(ws_ml + 2 * (cc2 * stride + qrow) + 1);
+            if (m2y > 0.0f) M = fmaxf(M, m2x);
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
+        if ((t & 63) == 0) hred[half][hw] = M;
+        __syncthreads();
+        M = fmaxf(hred[half][0], hred[half][1]);
+        __syncthreads();
+        float L = 0.0f;
+        for (int cc2 = t; cc2 < nsplit; cc2 += kD) {
+            const float m2x = fetch(ws_ml + 2 * (cc2 * stride + qrow)), m2y = fetch(ws_ml + 2 * (cc2 * stride + qrow) + 1);
+            const float w = m2y > 0.0f ? fast_exp2(m2x - M) : 0.0f;
+            wts[cc2] = w;
+            L = fmaf(m2y, w, L);
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m);
+        if ((t & 63) == 0) hred[half][hw] = L;
+        __syncthreads();
+        L = hred[half][0] + hred[half][1];
+        float O = 0.0f;
+        int k = 0;
+        for (; k + 8 <= nsplit; k += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = fetch(ws_o + ((k + u) * stride + qrow) * kD + t);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) O = fmaf(v[u], wts[k + u], O);
+        }
+        for (; k < nsplit; ++k) O = fmaf(fetch(ws_o + (k * stride + qrow) * kD + t), wts[k], O);
+        if (live) {
+            const int64_t bs = qrow / a.nh;
+            const int hq = (int)(qrow % a.nh);
+            a.O[bs * a.ldo + hq * kD + t] = (__bf16)(L > 0.0f ? O / L : 0.0f);
+        }
+        __syncthreads();   // wts and hred are reused by the next pair of rows
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m));
-    if ((t & 63) == 0) red[t >> 6] = M;
-    __syncthreads();
-    M = fmaxf(red[0], red[1]);
-    __syncthreads();
-    float L = 0.0f;
-    for (int c = t; c < nsplit; c += kD) {
-        const float2 ml = *reinterpret_cast<const float2 *>(ws_ml + 2 * (c * stride + qrow));
-        const float w = ml.y > 0.0f ? fast_exp2(ml.x - M) : 0.0f;
-        wts[c] = w;
-        L = fmaf(ml.y, w, L);
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) L += __shfl_xor(L, m);
-    if ((t & 63) == 0) red[t >> 6] = L;
-    __syncthreads();
-    L = red[0] + red[1];
-    float O = 0.0f;
-    int c = 0;
-    for (; c + 8 <= nsplit; c += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = ws_o[((c + u) * stride + qrow) * kD + t];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) O = fmaf(v[u], wts[c + u], O);
-    }
-    for (; c < nsplit; ++c) O = fmaf(ws_o[(c * stride + qrow) * kD + t], wts[c], O);
-    const int64_t bs = qrow / a.nh;
-    const int hq = (int)(qrow % a.nh);
-    a.O[bs * a.ldo + hq * kD + t] = (__bf16)(L > 0.0f ? O / L : 0.0f);
+    if (threadIdx.x == 0) __hip_atomic_store(arrivals + bg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NR>
-hipError_t launch_decode(const AttnDev &d, int chunk, int nsplit, float *ws_o, float *ws_ml, hipStream_t s)
+hipError_t launch_decode(const AttnDev &d, int chunk, int nsplit, float *ws_o, float *ws_ml, unsigned *arrivals,
+                         hipStream_t s)
 {
     const int grid = d.Bs * d.nkv * nsplit;
-    hipLaunchKernelGGL((attn_decode_kernel<NR>), dim3(grid), dim3(256), 0, s, d, chunk, nsplit, ws_o, ws_ml);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(d.Bs * d.Sq * d.nh), dim3(kD), 0, s, d, nsplit, ws_o, ws_ml);
+    hipLaunchKernelGGL((attn_decode_kernel<NR>), dim3(grid), dim3(256), 0, s, d, chunk, nsplit, ws_o, ws_ml,
+                       arrivals);
     return hipGetLastError();
 }
 
@@ -556,13 +598,14 @@ hipError_t launch_attn_bf16(const AttnArgs &x, int num_cu, hipStream_t s)
         hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(256), 0, s, d, nqt, 2 * num_cu);
         return hipGetLastError();
     }
-    float *ws_o = static_cast<float *>(x.ws);
+    unsigned *arrivals = static_cast<unsigned *>(x.ws);
+    float *ws_o = reinterpret_cast<float *>(static_cast<char *>(x.ws) + p.partials_offset);
     float *ws_ml = ws_o + (size_t)p.nsplit * x.Bs * x.Sq * x.nh * kD;
     const int rows = d.G * d.Sq;
-    if (rows <= 1) return launch_decode<1>(d, p.chunk, p.nsplit, ws_o, ws_ml, s);
-    if (rows <= 2) return launch_decode<2>(d, p.chunk, p.nsplit, ws_o, ws_ml, s);
-    if (rows <= 4) return launch_decode<4>(d, p.chunk, p.nsplit, ws_o, ws_ml, s);
-    return launch_decode<8>(d, p.chunk, p.nsplit, ws_o, ws_ml, s);
+    if (rows <= 1) return launch_decode<1>(d, p.chunk, p.nsplit, ws_o, ws_ml, arrivals, s);
+    if (rows <= 2) return launch_decode<2>(d, p.chunk, p.nsplit, ws_o, ws_ml, arrivals, s);
+    if (rows <= 4) return launch_decode<4>(d, p.chunk, p.nsplit, ws_o, ws_ml, arrivals, s);
+    return launch_decode<8>(d, p.chunk, p.nsplit, ws_o, ws_ml, arrivals, s);
 }
 
 }  // namespace tpk

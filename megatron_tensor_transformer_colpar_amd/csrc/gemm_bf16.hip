@@ -100,7 +100,7 @@ struct Cfg {
 // 4j + i/4); the 4 k-rows x 64 bytes a half-wave reads then cover all 64
 // banks once.  A K-major operand's k-rows are range-checked like rows, so
 // K need not be a multiple of BK.
-template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY>
+template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY, bool NTS>
 __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 {
     using C_ = Cfg<BM, BN, BK, S, NW>;
@@ -361,9 +361,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 
     // epilogue: element v of accumulator (i, j) is C[m][n] with
     //   m = tile row base + lane%32,  n = tile column base + 8*(v/4) + 4*(lane/32) + v%4,
-    // so each lane owns runs of 4 consecutive columns.  The fp32 and plain
-    // bf16 epilogues regroup those runs through LDS into whole-line stores;
-    // the gated one stores each run (8 bytes) directly.
+    // so each lane owns runs of 4 consecutive columns.  Every epilogue
+    // regroups those runs through LDS into whole-line stores.
     const bool full = (m0 + BM <= g.M) && (n0 + BNO <= g.N);
     auto load_bias = [&](const __bf16 *bp, int nb, int q) __attribute__((always_inline)) {
         f32x4 v = f32x4{};
@@ -407,6 +406,8 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
                         f32x4 *const c = reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n);
                         if constexpr (EPI == EPI_ACC_F32)
                             *c = *c + x;   // accumulate (weight gradients over micro-batches)
+                        else if constexpr (NTS)
+                            __builtin_nontemporal_store(x, c);   // streamed past the caches (see launch_cfg)
                         else
                             *c = x;
                     }
@@ -414,34 +415,55 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
             }
         }
     } else if constexpr (GATED) {
+        // The gated tile (BM x BNO bf16) is staged whole in stage 0, then
+        // stored as whole rows.  Lane (frow, fhalf) of wave (wm, wn) holds,
+        // for accumulator row i and q in 0..3, output row wm*WTM + 32i + frow
+        // and columns wn*WTN/2 + 32j + 8q + 4*fhalf .. +3 (gate in tile j, up
+        // in tile j + TN/2): half of 16-byte chunk c = wn*WTN/16 + 4j + q of
+        // that row.  Chunk c of row r sits at slot c ^ (r % CPL), so the
+        // 8-byte writes of one instruction (32 rows, one chunk) and the
+        // row-wise 16-byte reads spread over the banks.
+        constexpr int CPL = BNO / 8;   // 16-byte chunks per output row
+        static_assert(BM * BNO * 2 <= STAGE * 16, "gated staging area");
+        static_assert((BM * CPL) % (64 * NW) == 0 && 64 % CPL == 0, "gated drain geometry");
         const __bf16 *const bias2_p = g.bias2[bt];
+        __syncthreads();   // every wave is done reading the last slice
 #pragma unroll
         for (int j = 0; j < TN / 2; ++j) {
-            const int nb = n0 + wn * (C_::WTN / 2) + j * 32 + 4 * fhalf;
-            f32x4 bg[4], bu[4];
+            const int cb = wn * (C_::WTN / 16) + 4 * j;   // chunk of q = 0
+            const int nb = n0 + 8 * cb + 4 * fhalf;       // this lane's first column for q = 0
+            f32x4 bgv[4], buv[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                bg[q] = load_bias(bias_p, nb, q);
-                bu[q] = load_bias(bias2_p, nb, q);
+                bgv[q] = load_bias(bias_p, nb, q);
+                buv[q] = load_bias(bias2_p, nb, q);
             }
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                const int m = m0 + wm * C_::WTM + i * 32 + frow;
-                if (!full && m >= g.M) continue;
+                const int r = wm * C_::WTM + 32 * i + frow;
+                const int ju = j + TN / 2;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int n = nb + 8 * q;
-                    if (!full && n >= g.N) continue;
                     const f32x4 ga = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                           acc[i][j][4 * q + 3]} + bg[q];
-                    const int ju = j + TN / 2;
+                                           acc[i][j][4 * q + 3]} + bgv[q];
                     const f32x4 up = f32x4{acc[i][ju][4 * q], acc[i][ju][4 * q + 1], acc[i][ju][4 * q + 2],
-                                           acc[i][ju][4 * q + 3]} + bu[q];
+                                           acc[i][ju][4 * q + 3]} + buv[q];
                     const bf16x4 y = {(__bf16)(act<EPI>(ga[0]) * up[0]), (__bf16)(act<EPI>(ga[1]) * up[1]),
                                       (__bf16)(act<EPI>(ga[2]) * up[2]), (__bf16)(act<EPI>(ga[3]) * up[3])};
-                    *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * ldc + n) = y;
+                    reinterpret_cast<u32x2 *>(st0 + r * CPL + ((cb + q) ^ (r % CPL)))[fhalf] =
+                        __builtin_bit_cast(u32x2, y);
                 }
             }
+        }
+        __syncthreads();
+        constexpr int RPI = 64 / CPL;   // output rows per store instruction
+#pragma unroll
+        for (int k = 0; k < BM * CPL / (64 * NW); ++k) {
+            const int r = (k * NW + wave) * RPI + lane / CPL, c = lane % CPL;
+            const u32x4 v = st0[r * CPL + (c ^ (r % CPL))];
+            const int m = m0 + r, n = n0 + 8 * c;
+            if (full || (m < g.M && n < g.N))
+                *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(Cbase) + (int64_t)m * ldc + n) = v;
         }
     } else {
         // bf16 output (and the kept GeLU input) leaves through LDS like the
@@ -533,7 +555,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     }
 }
 
-template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY>
+template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY, bool NTS = false>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s)
 {
     GemmDev g;
@@ -559,7 +581,7 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
     g.tiles_m = (int)((a.M + BM - 1) / BM);
     g.tiles_n = (int)((a.N + BNO - 1) / BNO);
     const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(NW * 64);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY, NTS>), grid, block, 0, s, g);
     return hipGetLastError();
 }
 
@@ -567,9 +589,20 @@ template <int BM, int BN, int BK, int S, int NW, bool IL>
 hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
 {
     constexpr bool gated_ok = Cfg<BM, BN, BK, S, NW>::TN % 2 == 0;
+    // A launch whose fp32 output exceeds half the 256 MB last-level cache
+    // (a row-parallel partial at 8192 tokens is 256 MiB) streams it out with
+    // non-temporal stores: it cannot stay cached for its consumer anyway,
+    // and cached stores leave the tiles' epilogues waiting on write-backs
+    // (on the prefill shape the row-parallel launch took 418-439 us against
+    // 450-474 us with cached stores, alternating builds on two boxes).
+    // Smaller outputs, such as the 2048-token block's four partials (128 MiB)
+    // that its reduce reads right after, stay cached.
+    const bool stream = (int64_t)a.batch * a.M * a.N * 4 > (int64_t(128) << 20);
     if (a.layout == LAYOUT_B_KMAJOR) {   // input gradients
         switch (epi) {
-        case EPI_STORE_F32: return launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 1>(a, s);
+        case EPI_STORE_F32:
+            return stream ? launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 1, true>(a, s)
+                          : launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 1>(a, s);
         case EPI_BIAS: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS, 1>(a, s);
         case EPI_GELU_GRAD_TANH: return launch_one<BM, BN, BK, S, NW, IL, EPI_GELU_GRAD_TANH, 1>(a, s);
         case EPI_GELU_GRAD_ERF: return launch_one<BM, BN, BK, S, NW, IL, EPI_GELU_GRAD_ERF, 1>(a, s);
@@ -585,7 +618,9 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
     }
     switch (epi) {
     case EPI_BIAS_GELU: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU, 0>(a, s);
-    case EPI_STORE_F32: return launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 0>(a, s);
+    case EPI_STORE_F32:
+        return stream ? launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 0, true>(a, s)
+                      : launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 0>(a, s);
     case EPI_BIAS_GELU_ERF: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU_ERF, 0>(a, s);
     case EPI_BIAS: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS, 0>(a, s);
     case EPI_GATED_TANH:

@@ -13,7 +13,9 @@ AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv)
 {
     AttnPlan p{};
     const int64_t rows = (int64_t)(nh / nkv) * Sq;
-    p.decode = rows <= kAttnDecRows;
+    // the split-key kernel needs one arrival counter per (sequence, key/value
+    // head) in the counter region; more pairs take the matrix-core kernel
+    p.decode = rows <= kAttnDecRows && Bs * nkv <= kAttnMaxArrivals;
     if (!p.decode) return p;
     // enough workgroups to cover the chip four times over (a workgroup
     // keeps only 16 KiB of its chunk in flight), at most kAttnDecMaxChunk keys
@@ -32,8 +34,12 @@ AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv)
     }
     p.nsplit = (int)nsplit;
     p.chunk = (int)chunk;
+    // the arrival counters first, in a region of fixed size (so that no
+    // call's partials ever cover another call's counters), then the chunks'
+    // partials (weighted values, then max and sum per row)
     const int64_t qrows = Bs * Sq * nh;
-    p.ws_bytes = (size_t)(nsplit * qrows * (kAttnD + 2) * 4);
+    p.partials_offset = (size_t)kAttnMaxArrivals * 4;
+    p.ws_bytes = p.partials_offset + (size_t)(nsplit * qrows * (kAttnD + 2) * 4);
     return p;
 }
 

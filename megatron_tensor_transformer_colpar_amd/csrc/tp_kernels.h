@@ -85,12 +85,14 @@ struct AttnPlan {
     bool decode;
     int nsplit, chunk;
     size_t ws_bytes;
+    size_t partials_offset;   // the workspace: arrival counters at 0, the partials from here
 };
 AttnPlan attn_plan(int64_t Bs, int64_t Sq, int64_t Lk, int nh, int nkv);
 constexpr int kAttnD = 128;             // head dim
 constexpr int kAttnDecRows = 8;         // most query rows per key/value head on the decode kernel
 constexpr int kAttnDecMaxChunk = 512;   // most keys per decode workgroup
 constexpr int kAttnMaxSplit = 4096;     // most key chunks per sequence on the decode path
+constexpr int kAttnMaxArrivals = 4096;  // most (sequence, key/value head) pairs on the decode path
 hipError_t launch_attn_bf16(const AttnArgs &a, int num_cu, hipStream_t s);
 
 

@@ -386,7 +386,12 @@ def test_attn_workspace_bytes():
     # prefill shapes need none; the split-key decode path needs its partials
     assert tp.tp_attn_workspace_bytes(4, 2048, 2048, 8, 8) == 0
     n = tp.tp_attn_workspace_bytes(8, 1, 2048, 8, 8)
-    assert n > 0 and n % (8 * 8 * 130 * 4) == 0
+    # 4096 arrival counters (16 KiB), then the partials of 8 x 8 query rows
+    # (128 weighted dims, max and sum) per chunk
+    assert n > 16384 and (n - 16384) % (8 * 8 * 130 * 4) == 0
+    # more (sequence, key/value head) pairs than counters: the prefill kernel, no workspace
+    assert tp.tp_attn_workspace_bytes(512, 1, 2048, 8, 8) > 0
+    assert tp.tp_attn_workspace_bytes(513, 1, 2048, 8, 8) == 0
     assert tp.tp_attn_workspace_bytes(0, 1, 2048, 8, 8) == 0
     assert tp.tp_attn_workspace_bytes(1, 1, 2048, 8, 3) == 0     # invalid grouping
     assert attn(Bs=8, Sq=1, Lk=2048, ws=P[5], ws_bytes=n - 4) == tp.TP_ERR_SHAPE
