@@ -31,14 +31,18 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
 
 // GeLU, tanh form (Hendrycks & Gimpel, arXiv:1606.08415):
 //   g(x) = x/2 * (1 + tanh(u)),  u = sqrt(2/pi) * (x + 0.044715 x^3).
-// Evaluated through (1 + tanh u)/2 = 1/(1 + exp(-2u)), so one exp and one
-// reciprocal; exp comes from the device library.  The limits are right:
-// x -> -inf gives exp -> inf and g -> -0; x -> +inf gives g -> x.
+// Evaluated through (1 + tanh u)/2 = 1/(1 + e^(-2u)) = 1/(1 + 2^z) with
+// z = x (c1 + c2 x^2), c1 = -2 sqrt(2/pi) log2(e), c2 = 0.044715 c1: a
+// square, one fma and one multiply, the hardware exp2 and reciprocal, an add
+// and a multiply (two fewer vector instructions per element than forming u
+// and exp(-2u); this epilogue is bound by them).  The limits are right:
+// x -> -inf gives 2^z -> inf and g -> -0; x -> +inf gives g -> x.
 __device__ __forceinline__ float gelu_tanh(float x)
 {
-    const float two_k = 1.5957691216057308f;  // 2 * sqrt(2/pi)
-    const float v = two_k * x * (1.0f + 0.044715f * x * x);
-    return __fdividef(x, 1.0f + __expf(-v));
+    constexpr float c1 = -2.302208198144325f;    // -2 sqrt(2/pi) log2(e)
+    constexpr float c2 = -0.1029432395800235f;   // 0.044715 * c1
+    const float e = __builtin_amdgcn_exp2f(x * fmaf(c2, x * x, c1));
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // GeLU, exact form (Hendrycks & Gimpel): g(x) = x * Phi(x)
