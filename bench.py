@@ -65,9 +65,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha(name):
-    p = os.path.join(ROOT, "megatron_tensor_transformer_colpar_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+# the sources the prefill GEMM kernels are compiled from
+GEMM_SOURCES = ["gemm_bf16.hip", "device_common.h", "tp_kernels.h"]
+
+
+def source_sha(names):
+    """Hash of one source file, or of a list of them (in order)."""
+    h = hashlib.sha256()
+    for name in ([names] if isinstance(names, str) else names):
+        h.update(open(os.path.join(ROOT, "megatron_tensor_transformer_colpar_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_key):
@@ -870,7 +877,7 @@ def write_traffic(prof_dir):
         out = {}
     for key, k in kern.items():
         fr, wr = sum(F[k]) / len(F[k]), sum(W[k]) / len(W[k])
-        out[key + "@prefill"] = {"source": "gemm_bf16.hip", "source_sha": source_sha("gemm_bf16.hip"),
+        out[key + "@prefill"] = {"source": GEMM_SOURCES, "source_sha": source_sha(GEMM_SOURCES),
                                  "kernel": k, "fetch_kib_raw": round(fr), "write_kib_raw": round(wr),
                                  "fetch_bytes": round(fr * 1024 * sf), "write_bytes": round(wr * 1024 * sw),
                                  "scale": {"fetch": sf, "write": sw}, "algorithmic_bytes": alg[key],

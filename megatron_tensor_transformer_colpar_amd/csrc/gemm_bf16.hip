@@ -27,6 +27,8 @@
 //    lgkmcnt(0) so no wave still reads a stage when it is refilled) followed
 //    by a bare s_barrier: a __syncthreads() fence would also drain the
 //    loads still in flight for later slices.
+#include <type_traits>
+
 #include "device_common.h"
 #include "tp_kernels.h"
 
@@ -71,18 +73,22 @@ __host__ __device__ constexpr int wait_vm_lgkm0(int vm)
     return (vm & 0xF) | (0x7 << 4) | (0x0 << 8) | ((vm >> 4) << 14);
 }
 
-template <int BM, int BN, int BK, int S, int NW>
+template <int BM, int BN, int BK, int S, int NW, int MF = 32>
 struct Cfg {
     static constexpr int WN = NW / 2;                  // waves along N (2 along M)
     static constexpr int WTM = BM / 2, WTN = BN / WN;  // wave tile
-    static constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA tiles per wave
+    static constexpr int TM = WTM / MF, TN = WTN / MF; // MF x MF accumulator tiles per wave
     static constexpr int CH = BK / 8;                  // 16-byte chunks per LDS row
     static constexpr int RB = 64 / CH;                 // rows per 1 KiB DMA block
-    static constexpr int KQ = BK / 16;                 // MFMA k-steps per slice
+    static constexpr int KM = MF == 32 ? 16 : 32;      // k per MFMA instruction
+    static constexpr int KQ = BK / KM;                 // MFMA k-steps per slice
+    static constexpr int CPQ = KM / 8;                 // 16-byte chunks of a row per k-step
     static constexpr int A_LD = BM / RB / NW, B_LD = BN / RB / NW;  // DMA instrs per wave per slice
     static constexpr int LOADS = A_LD + B_LD;          // per thread per slice
     static constexpr int STAGE = (BM + BN) * CH;       // 16-byte slots per stage
     static_assert(BK == 32 || BK == 64, "BK");
+    static_assert(MF == 16 || MF == 32, "MFMA shape");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tiles are whole 32x32 blocks");
     static_assert(S >= 2 && S <= 5, "stages");
     static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the DMA layout");
     static_assert((S - 2) * LOADS <= 63, "vmcnt range");
@@ -100,13 +106,31 @@ struct Cfg {
 // 4j + i/4); the 4 k-rows x 64 bytes a half-wave reads then cover all 64
 // banks once.  A K-major operand's k-rows are range-checked like rows, so
 // K need not be a multiple of BK.
-template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY, bool NTS>
+// The order of one 16x16x32 k-step, row by row: TN MFMAs, then the row's
+// fragment reads (its A fragment, and B fragment i while i < TN), then (RF)
+// its share of the refill DMA.
+template <int I, int TM, int TN, int DPR, int LOADS, bool RF>
+__device__ __forceinline__ void pin_rows16()
+{
+    if constexpr (I < TM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, I < TN ? 2 : 1, 0);
+        if constexpr (RF && I * DPR < LOADS)
+            __builtin_amdgcn_sched_group_barrier(0x020, ((I + 1) * DPR < LOADS ? (I + 1) * DPR : LOADS) - I * DPR, 0);
+        pin_rows16<I + 1, TM, TN, DPR, LOADS, RF>();
+    }
+}
+
+template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY, bool NTS, int MF>
 __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 {
-    using C_ = Cfg<BM, BN, BK, S, NW>;
+    using C_ = Cfg<BM, BN, BK, S, NW, MF>;
     constexpr int TM = C_::TM, TN = C_::TN, STAGE = C_::STAGE, CH = C_::CH, RB = C_::RB, KQ = C_::KQ;
     constexpr bool AKM = LAY == 2, BKM = LAY >= 1;   // K-major operands
-    static_assert(!(AKM || BKM) || (BK == 64 && BM >= 128 && BN >= 128 && NW % 2 == 0), "K-major tile shape");
+    static_assert(!(AKM || BKM) || (BK == 64 && BM >= 128 && BN >= 128 && NW % 2 == 0 && MF == 32),
+                  "K-major tile shape");
+    static_assert(MF == 32 || !epi_act_grad(EPI), "the gradient epilogues run with 32x32 tiles");
+    using AccT = typename std::conditional<MF == 32, f32x16, f32x4>::type;
     // Gated: each wave's WTN rows of the B tile are WTN/2 gate rows followed
     // by the matching WTN/2 up rows, so accumulator tiles j and j + TN/2 of a
     // lane hold gate and up of the same output elements; a tile then covers
@@ -186,10 +210,13 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     // The row offset stays in the per-lane voffset, which the buffer range
     // check covers, so rows past M or N read zero; the in-row K offset goes
     // in soffset.  Refills past the last slice re-read the last slice.
-    auto issue = [&](u32x4 *stage, int kt) __attribute__((always_inline)) {
+    // issue_part(stage, kt, lo, hi) issues DMA instructions lo .. hi-1 of a
+    // slice (the A_LD instructions of the A tile, then the B_LD of the B tile).
+    auto issue_part = [&](u32x4 *stage, int kt, int lo, int hi) __attribute__((always_inline)) {
         const uint32_t koff = (uint32_t)min(kt, KT - 1) * (BK * 2);
 #pragma unroll
         for (int j = 0; j < C_::A_LD; ++j) {
+            if (j < lo || j >= hi) continue;
             if constexpr (AKM) {
                 const uint32_t vo = ak_voff + j * ak_jstep + (uint32_t)min(kt, KT - 1) * (uint32_t)(BK * g.lda * 2);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(stage + (NW * j + wave) * 64), 16, vo, 0, 0, 0);
@@ -199,6 +226,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         }
 #pragma unroll
         for (int j = 0; j < C_::B_LD; ++j) {
+            if (C_::A_LD + j < lo || C_::A_LD + j >= hi) continue;
             if constexpr (BKM) {
                 const uint32_t vo = bk_voff + j * bk_jstep + (uint32_t)min(kt, KT - 1) * (uint32_t)(BK * g.ldb * 2);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16, vo,
@@ -218,10 +246,16 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
                                                         b_voff + j * b_jstep, koff, 0, 0);
         }
     };
+    auto issue = [&](u32x4 *stage, int kt) __attribute__((always_inline)) { issue_part(stage, kt, 0, C_::LOADS); };
 
-    // fragment geometry: lane reads row (lane & 31) of each 32-row tile,
-    // K chunk 2*q + (lane >> 5) of the slice
-    const int frow = lane & 31, fhalf = lane >> 5, fsw = swz<CH>(frow);
+    // fragment geometry: lane reads row (lane % MF) of each MF-row tile,
+    // K chunk CPQ*q + lane/MF of the slice (32x32x16: 16 k per step, lanes
+    // 0-31 and 32-63 take 8 each; 16x16x32: 32 k per step, four groups of 16
+    // lanes take 8 each).  The swizzle keeps both reads conflict-free: a
+    // 16-lane group reads 16 consecutive rows of one logical chunk, which
+    // c ^ swz(row) spreads over all 64 banks.
+    const int frow = lane % MF, fq = lane / MF, fsw = swz<CH>(frow);
+    const int fhalf = lane >> 5;   // 32x32 tiles: the lane's k half (also its column half in the result)
     const int a_base = (wm * C_::WTM + frow) * CH;
     const int b_base = (BM + wn * C_::WTN + frow) * CH;
 
@@ -250,38 +284,45 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 
     bf16x8 fa[2][TM], fb[2][TN];
     auto read_frags = [&](const u32x4 *stage, int q, int p) __attribute__((always_inline)) {
-        const int slot = (2 * q + fhalf) ^ fsw;
+        const int slot = (C_::CPQ * q + fq) ^ fsw;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if constexpr (AKM)
                 fa[p][i] = tr_frag(stage, BM * 2, a_tr[i], q);
             else
-                fa[p][i] = __builtin_bit_cast(bf16x8, stage[a_base + i * 32 * CH + slot]);
+                fa[p][i] = __builtin_bit_cast(bf16x8, stage[a_base + i * MF * CH + slot]);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             if constexpr (BKM)
                 fb[p][j] = tr_frag(stage + BM * CH, BN * 2, b_tr[j], q);
             else
-                fb[p][j] = __builtin_bit_cast(bf16x8, stage[b_base + j * 32 * CH + slot]);
+                fb[p][j] = __builtin_bit_cast(bf16x8, stage[b_base + j * MF * CH + slot]);
         }
     };
 
-    f32x16 acc[TM][TN];
+    AccT acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < TN; ++j) acc[i][j] = AccT{};
 
-    // B is the MFMA's first operand, so the 32x32 result is the tile
-    // transposed: lane l ends up with 4 consecutive columns of row l%32,
-    // which the epilogue stores as one vector.
+    // B is the MFMA's first operand, so the result is the tile transposed:
+    // lane l ends up with runs of 4 consecutive columns of row l%MF, which
+    // the epilogue handles as vectors.  16x16x32 draws less power per flop
+    // than 32x32x16: a register-only loop on bf16 data of this kind, two
+    // waves per SIMD, sustains 1.97 PFLOP/s at 1972 MHz against 1.77 PFLOP/s
+    // at 1767 MHz, both with the matrix cores 95% busy (MI355X, power-capped).
     auto mfmas = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[p][j], fa[p][i], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (MF == 32)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[p][j], fa[p][i], acc[i][j], 0, 0, 0);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[p][j], fa[p][i], acc[i][j], 0, 0, 0);
+            }
     };
 
     // Each phase issues the next k-step's fragment reads and the current
@@ -339,6 +380,44 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         phase_refill(cur, kt + S, nxt, 0, (KQ - 1) & 1);
     };
 
+    // 16x16x32 tiles: a wave's fragments of both buffers would not fit
+    // beside its 128 accumulator registers (two waves per SIMD), so the A
+    // fragments are single-buffered: A fragment i of the next k-step is read
+    // right after the MFMAs of row i (its last use) are issued; the B
+    // fragments stay double-buffered.  Each row of MFMAs is followed by its
+    // reads and, in the step after the barrier, by its share of the refill
+    // DMA; sched_group_barriers pin that order.
+    static_assert(MF == 32 || (KQ == 2 && TN <= TM && !AKM && !BKM), "16x16x32 main loop shape");
+    constexpr int DPR = (C_::LOADS + TM - 1) / TM;   // refill DMA instructions per row
+    auto step16 = [&](auto refill_tag, const u32x4 *rstage, int rq, int pm, int pr, u32x4 *refill,
+                      int kt_refill) __attribute__((always_inline)) {
+        constexpr bool RF = decltype(refill_tag)::value;
+        if constexpr (MF == 16) {
+            const int slot = (C_::CPQ * rq + fq) ^ fsw;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[pm][j], fa[0][i], acc[i][j], 0, 0, 0);
+                fa[0][i] = __builtin_bit_cast(bf16x8, rstage[a_base + i * MF * CH + slot]);
+                if (i < TN) fb[pr][i] = __builtin_bit_cast(bf16x8, rstage[b_base + i * MF * CH + slot]);
+                if constexpr (RF) issue_part(refill, kt_refill, i * DPR, min((i + 1) * DPR, C_::LOADS));
+            }
+            pin_rows16<0, TM, TN, DPR, C_::LOADS, RF>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // one K slice in `cur`: k-step 0 (reading k-step 1 of `cur`), the
+    // barrier that publishes `nxt`, k-step 1 (reading k-step 0 of `nxt`,
+    // refilling `cur` with slice kt + S)
+    auto slice16 = [&](u32x4 *cur, u32x4 *nxt, int kt) __attribute__((always_inline)) {
+        step16(std::false_type{}, cur, 1, 0, 1, cur, 0);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 2) * C_::LOADS));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        step16(std::true_type{}, nxt, 0, 1, 0, cur, kt + S);
+    };
+
     u32x4 *const ring[5] = {st0, st1, st2, st3, st4};
 
     // prologue: slices 0 .. S-1 in flight, slice 0 landed and published
@@ -346,62 +425,115 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     for (int r = 0; r < S; ++r) issue(ring[r], r);
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 1) * C_::LOADS));
     __builtin_amdgcn_s_barrier();
-    read_frags(st0, 0, 0);
+    if constexpr (MF == 16) {
+        // the first k-step's fragments, read in the order step16 reads them,
+        // so that the waits the compiler places at the top of the main loop
+        // (merged over its entry and its back edge) name the reads they need
+        const int slot0 = fq ^ fsw;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            fa[0][i] = __builtin_bit_cast(bf16x8, st0[a_base + i * MF * CH + slot0]);
+            if (i < TN) fb[0][i] = __builtin_bit_cast(bf16x8, st0[b_base + i * MF * CH + slot0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    } else {
+        read_frags(st0, 0, 0);
+    }
 
     int kt = 0;
     for (; kt + S <= KT; kt += S) {
 #pragma unroll
-        for (int r = 0; r < S; ++r) slice(ring[r], ring[(r + 1) % S], kt + r);
+        for (int r = 0; r < S; ++r) {
+            if constexpr (MF == 16)
+                slice16(ring[r], ring[(r + 1) % S], kt + r);
+            else
+                slice(ring[r], ring[(r + 1) % S], kt + r);
+        }
     }
 #pragma unroll
     for (int r = 0; r + 1 < S; ++r)
-        if (kt + r < KT) slice(ring[r], ring[r + 1], kt + r);
+        if (kt + r < KT) {
+            if constexpr (MF == 16)
+                slice16(ring[r], ring[r + 1], kt + r);
+            else
+                slice(ring[r], ring[r + 1], kt + r);
+        }
     // drain the clamped refills before the workgroup exits
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
-    // epilogue: element v of accumulator (i, j) is C[m][n] with
-    //   m = tile row base + lane%32,  n = tile column base + 8*(v/4) + 4*(lane/32) + v%4,
-    // so each lane owns runs of 4 consecutive columns.  Every epilogue
-    // regroups those runs through LDS into whole-line stores.
+    // Epilogue.  The accumulators are read as runs of 4 consecutive output
+    // columns of one row: per 32-row band I of the wave tile (WTM/32 bands)
+    // a lane holds RUNS = WTN/8 runs, run u covering band row run_row(u) and
+    // columns 8*run_chunk(u) + 4*run_half(u) .. +3 of the wave tile, i.e.
+    // half run_half(u) of 16-byte bf16 chunk run_chunk(u) of that row.
+    //   32x32 tiles: run u = 4j + q is acc[I][j][4q .. 4q+3], row lane%32,
+    //                columns 32j + 8q + 4(lane/32);
+    //   16x16 tiles: run u = a*TN + j is acc[2I + a][j], row 16a + lane%16,
+    //                columns 16j + 4(lane/16).
+    // Every epilogue regroups the runs through LDS into whole-line stores.
+    constexpr int RUNS = C_::WTN / 8, BANDS = C_::WTM / 32;
+    auto run = [&](int I, int u) __attribute__((always_inline)) {
+        if constexpr (MF == 32) {
+            const int j = u / 4, q = u % 4;
+            return f32x4{acc[I][j][4 * q], acc[I][j][4 * q + 1], acc[I][j][4 * q + 2], acc[I][j][4 * q + 3]};
+        } else {
+            return acc[2 * I + u / TN][u % TN];
+        }
+    };
+    auto run_row = [&](int u) __attribute__((always_inline)) {
+        return MF == 32 ? (lane & 31) : 16 * (u / TN) + (lane & 15);
+    };
+    auto run_chunk = [&](int u) __attribute__((always_inline)) {
+        return MF == 32 ? u : 2 * (u % TN) + (lane >> 5);
+    };
+    auto run_half = [&](int u) __attribute__((always_inline)) {
+        return MF == 32 ? (lane >> 5) : ((lane >> 4) & 1);
+    };
     const bool full = (m0 + BM <= g.M) && (n0 + BNO <= g.N);
-    auto load_bias = [&](const __bf16 *bp, int nb, int q) __attribute__((always_inline)) {
+    // 4 bias values at column n (zeros past N or without a bias)
+    auto load_bias4 = [&](const __bf16 *bp, int n) __attribute__((always_inline)) {
         f32x4 v = f32x4{};
-        if (bp && (full || nb + 8 * q < g.N)) {
-            const bf16x4 b4 = *reinterpret_cast<const bf16x4 *>(bp + nb + 8 * q);
+        if (bp && (full || n < g.N)) {
+            const bf16x4 b4 = *reinterpret_cast<const bf16x4 *>(bp + n);
             v = f32x4{(float)b4[0], (float)b4[1], (float)b4[2], (float)b4[3]};
         }
         return v;
     };
     if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) {
-        // fp32 output leaves through LDS, one 32x32 accumulator tile at a time
-        // per wave (4 KiB each, inside stage 0), so that every store
-        // instruction writes 8 rows x 128 contiguous bytes, i.e. whole lines.
-        // Stored straight from the accumulators, an instruction wrote 32 bytes
-        // in each of 32 rows; on the 4-shard row-parallel launch at 2048
-        // tokens that took 261 us against 247 us like this.
-        // Rows of the staging tile are 8 chunks of 4 floats; chunk c of row r
-        // sits at slot c ^ swz(r), which keeps both the column-wise write and
-        // the row-wise read conflict-free.  A wave's LDS operations complete
-        // in issue order, so no wait separates its writes from its reads or
-        // one tile's reads from the next tile's writes.
+        // fp32 output leaves through LDS, one 32x32 block (a band's columns
+        // 32J .. 32J+31) at a time per wave (4 KiB each, inside stage 0), so
+        // that every store instruction writes 8 rows x 128 contiguous bytes,
+        // i.e. whole lines.  Stored straight from the accumulators, an
+        // instruction wrote 32 bytes in each of 32 rows; on the 4-shard
+        // row-parallel launch at 2048 tokens that took 261 us against 247 us
+        // like this.  Rows of the staging block are 8 chunks of 4 floats;
+        // chunk c of row r sits at slot c ^ swz(r), which keeps both the
+        // column-wise write and the row-wise read conflict-free.  A wave's
+        // LDS operations complete in issue order, so no wait separates its
+        // writes from its reads or one block's reads from the next block's
+        // writes.
         static_assert(NW * 32 * 32 * 4 <= STAGE * 16, "epilogue staging area");
         __syncthreads();   // every wave is done reading the last slice
         float *const stg = reinterpret_cast<float *>(st0) + wave * 32 * 32;
         const int mw = m0 + wm * C_::WTM, nw = n0 + wn * C_::WTN;
         const int rrow = lane >> 3, rch = lane & 7;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+        for (int I = 0; I < BANDS; ++I) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
+            for (int J = 0; J < C_::WTN / 32; ++J) {
+                // the 4 runs of this lane in block J: 32x32 tiles u = 4J .. 4J+3;
+                // 16x16 tiles tile columns 2J, 2J+1 of both 16-row halves
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<f32x4 *>(stg + frow * 32 + 4 * ((2 * q + fhalf) ^ swz<8>(frow))) =
-                        f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                for (int w = 0; w < 4; ++w) {
+                    const int u = MF == 32 ? 4 * J + w : (w / 2) * TN + 2 * J + (w % 2);
+                    const int r = run_row(u), c = 2 * run_chunk(u) + run_half(u) - 8 * J;
+                    *reinterpret_cast<f32x4 *>(stg + r * 32 + 4 * (c ^ swz<8>(r))) = run(I, u);
+                }
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int r = 8 * rr + rrow;
                     const f32x4 x = *reinterpret_cast<const f32x4 *>(stg + r * 32 + 4 * (rch ^ swz<8>(r)));
-                    const int m = mw + 32 * i + r, n = nw + 32 * j + 4 * rch;
+                    const int m = mw + 32 * I + r, n = nw + 32 * J + 4 * rch;
                     if (full || (m < g.M && n < g.N)) {
                         f32x4 *const c = reinterpret_cast<f32x4 *>(static_cast<float *>(Cbase) + (int64_t)m * ldc + n);
                         if constexpr (EPI == EPI_ACC_F32)
@@ -416,43 +548,34 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         }
     } else if constexpr (GATED) {
         // The gated tile (BM x BNO bf16) is staged whole in stage 0, then
-        // stored as whole rows.  Lane (frow, fhalf) of wave (wm, wn) holds,
-        // for accumulator row i and q in 0..3, output row wm*WTM + 32i + frow
-        // and columns wn*WTN/2 + 32j + 8q + 4*fhalf .. +3 (gate in tile j, up
-        // in tile j + TN/2): half of 16-byte chunk c = wn*WTN/16 + 4j + q of
-        // that row.  Chunk c of row r sits at slot c ^ (r % CPL), so the
-        // 8-byte writes of one instruction (32 rows, one chunk) and the
-        // row-wise 16-byte reads spread over the banks.
+        // stored as whole rows.  A wave's WTN accumulator columns are WTN/2
+        // gate columns followed by the matching WTN/2 up columns, so gate run
+        // u (in the first half) pairs with up run u + RUNS/2 (32x32 tiles) or
+        // u + TN/2 (16x16 tiles); the pair gives output row wm*WTM + 32I +
+        // run_row(u), chunk wn*WTN/16 + run_chunk(u), half run_half(u).
+        // Chunk c of row r sits at slot c ^ (r % CPL), so the 8-byte writes
+        // of one instruction and the row-wise 16-byte reads spread over the
+        // banks.
         constexpr int CPL = BNO / 8;   // 16-byte chunks per output row
         static_assert(BM * BNO * 2 <= STAGE * 16, "gated staging area");
         static_assert((BM * CPL) % (64 * NW) == 0 && 64 % CPL == 0, "gated drain geometry");
         const __bf16 *const bias2_p = g.bias2[bt];
         __syncthreads();   // every wave is done reading the last slice
 #pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-            const int cb = wn * (C_::WTN / 16) + 4 * j;   // chunk of q = 0
-            const int nb = n0 + 8 * cb + 4 * fhalf;       // this lane's first column for q = 0
-            f32x4 bgv[4], buv[4];
+        for (int u = 0; u < RUNS; ++u) {
+            const bool gate = MF == 32 ? u < RUNS / 2 : (u % TN) < TN / 2;
+            if (!gate) continue;
+            const int uu = MF == 32 ? u + RUNS / 2 : u + TN / 2;
+            const int c = wn * (C_::WTN / 16) + run_chunk(u);
+            const int n = n0 + 8 * c + 4 * run_half(u);
+            const f32x4 bgv = load_bias4(bias_p, n), buv = load_bias4(bias2_p, n);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                bgv[q] = load_bias(bias_p, nb, q);
-                buv[q] = load_bias(bias2_p, nb, q);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm * C_::WTM + 32 * i + frow;
-                const int ju = j + TN / 2;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 ga = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                           acc[i][j][4 * q + 3]} + bgv[q];
-                    const f32x4 up = f32x4{acc[i][ju][4 * q], acc[i][ju][4 * q + 1], acc[i][ju][4 * q + 2],
-                                           acc[i][ju][4 * q + 3]} + buv[q];
-                    const bf16x4 y = {(__bf16)(act<EPI>(ga[0]) * up[0]), (__bf16)(act<EPI>(ga[1]) * up[1]),
-                                      (__bf16)(act<EPI>(ga[2]) * up[2]), (__bf16)(act<EPI>(ga[3]) * up[3])};
-                    reinterpret_cast<u32x2 *>(st0 + r * CPL + ((cb + q) ^ (r % CPL)))[fhalf] =
-                        __builtin_bit_cast(u32x2, y);
-                }
+            for (int I = 0; I < BANDS; ++I) {
+                const int r = wm * C_::WTM + 32 * I + run_row(u);
+                const f32x4 ga = run(I, u) + bgv, up = run(I, uu) + buv;
+                const bf16x4 y = {(__bf16)(act<EPI>(ga[0]) * up[0]), (__bf16)(act<EPI>(ga[1]) * up[1]),
+                                  (__bf16)(act<EPI>(ga[2]) * up[2]), (__bf16)(act<EPI>(ga[3]) * up[3])};
+                reinterpret_cast<u32x2 *>(st0 + r * CPL + (c ^ (r % CPL)))[run_half(u)] = __builtin_bit_cast(u32x2, y);
             }
         }
         __syncthreads();
@@ -467,89 +590,78 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         }
     } else {
         // bf16 output (and the kept GeLU input) leaves through LDS like the
-        // fp32 output: a wave stages its 32 x WTN block of one accumulator
-        // row i (TN 16-byte chunks of 8 values per 32 columns; a lane puts
-        // its 4 values of chunk 4j + q into half fhalf of the slot), then
-        // reads it back row-wise, so a store instruction writes 64/CHR rows
-        // x CHR*16 contiguous bytes: whole 128-byte lines when WTN = 64.
-        constexpr int CHR = TN * 4, RPI = 64 / CHR;
+        // fp32 output: a wave stages its 32 x WTN block of one band (a lane
+        // puts run u into half run_half(u) of chunk run_chunk(u) of row
+        // run_row(u)), then reads it back row-wise, so a store instruction
+        // writes 64/CHR rows x CHR*16 contiguous bytes: whole 128-byte lines
+        // when WTN = 64.
+        constexpr int CHR = RUNS, RPI = 64 / CHR;
         static_assert(NW * 32 * CHR <= STAGE, "epilogue staging area");
         __syncthreads();   // every wave is done reading the last slice
         u32x4 *const stg = st0 + wave * 32 * CHR;
         const int mw = m0 + wm * C_::WTM, nw = n0 + wn * C_::WTN;
-        f32x4 bias[TN][4];
+        f32x4 bias[RUNS];
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                bias[j][q] = epi_has_bias(EPI) ? load_bias(bias_p, nw + j * 32 + 4 * fhalf, q) : f32x4{};
-        auto put = [&](int j, int q, f32x4 v) __attribute__((always_inline)) {
+        for (int u = 0; u < RUNS; ++u)
+            bias[u] = epi_has_bias(EPI) ? load_bias4(bias_p, nw + 8 * run_chunk(u) + 4 * run_half(u)) : f32x4{};
+        auto put = [&](int u, f32x4 v) __attribute__((always_inline)) {
             const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
-            reinterpret_cast<u32x2 *>(stg + frow * CHR + ((4 * j + q) ^ swz<CHR>(frow)))[fhalf] =
+            const int r = run_row(u);
+            reinterpret_cast<u32x2 *>(stg + r * CHR + (run_chunk(u) ^ swz<CHR>(r)))[run_half(u)] =
                 __builtin_bit_cast(u32x2, b);
         };
-        auto drain = [&](__bf16 *dst, int64_t ld, int i) __attribute__((always_inline)) {
+        auto drain = [&](__bf16 *dst, int64_t ld, int I) __attribute__((always_inline)) {
 #pragma unroll
             for (int rr = 0; rr < CHR / 2; ++rr) {
                 const int r = RPI * rr + lane / CHR, c = lane % CHR;
                 const u32x4 v = stg[r * CHR + (c ^ swz<CHR>(r))];
-                const int m = mw + 32 * i + r, n = nw + 8 * c;
+                const int m = mw + 32 * I + r, n = nw + 8 * c;
                 if (full || (m < g.M && n < g.N)) *reinterpret_cast<u32x4 *>(dst + (int64_t)m * ld + n) = v;
             }
         };
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            auto xv = [&](int j, int q) __attribute__((always_inline)) {
-                return f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            };
+        for (int I = 0; I < BANDS; ++I) {
             if constexpr (epi_act_grad(EPI)) {
-                // gradient at the GeLU input: x * g'(u), u the saved GeLU input
+                // gradient at the GeLU input: x * g'(u), u the saved GeLU input.
                 // u's rows arrive the way the output leaves: whole lines,
-                // row-wise into the slot, then each lane takes its values
-                // (read straight into the accumulator layout, a load touched
-                // 16 bytes in each of 32 rows; dU at 2048 tokens 69.6 -> 68.7 us)
-                bf16x4 uv[TN][4];
+                // row-wise into the slot, then each lane takes its runs (read
+                // straight into the accumulator layout, a load touched 16 bytes
+                // in each of 32 rows; dU at 2048 tokens 69.6 -> 68.7 us)
+                bf16x4 uv[RUNS];
 #pragma unroll
                 for (int rr = 0; rr < CHR / 2; ++rr) {
                     const int r = RPI * rr + lane / CHR, c = lane % CHR;
-                    const int mr = mw + 32 * i + r, n = nw + 8 * c;
+                    const int mr = mw + 32 * I + r, n = nw + 8 * c;
                     u32x4 v = {};
                     if (full || (mr < g.M && n < g.N))
                         v = *reinterpret_cast<const u32x4 *>(aux_p + (int64_t)mr * g.ldaux + n);
                     stg[r * CHR + (c ^ swz<CHR>(r))] = v;
                 }
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+                for (int u = 0; u < RUNS; ++u) {
+                    const int r = run_row(u);
+                    uv[u] = __builtin_bit_cast(
+                        bf16x4, reinterpret_cast<const u32x2 *>(stg + r * CHR + (run_chunk(u) ^ swz<CHR>(r)))[run_half(u)]);
+                }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        uv[j][q] = __builtin_bit_cast(
-                            bf16x4, reinterpret_cast<const u32x2 *>(stg + frow * CHR + ((4 * j + q) ^ swz<CHR>(frow)))[fhalf]);
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const bf16x4 u = uv[j][q];
-                        const f32x4 x = xv(j, q);
-                        put(j, q, f32x4{x[0] * act_grad<EPI>((float)u[0]), x[1] * act_grad<EPI>((float)u[1]),
-                                        x[2] * act_grad<EPI>((float)u[2]), x[3] * act_grad<EPI>((float)u[3])});
-                    }
-                drain(static_cast<__bf16 *>(Cbase), ldc, i);
+                for (int u = 0; u < RUNS; ++u) {
+                    const f32x4 x = run(I, u);
+                    put(u, f32x4{x[0] * act_grad<EPI>((float)uv[u][0]), x[1] * act_grad<EPI>((float)uv[u][1]),
+                                 x[2] * act_grad<EPI>((float)uv[u][2]), x[3] * act_grad<EPI>((float)uv[u][3])});
+                }
+                drain(static_cast<__bf16 *>(Cbase), ldc, I);
             } else {
                 if (aux_p) {   // keep the GeLU input for the backward pass
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) put(j, q, xv(j, q) + bias[j][q]);
-                    drain(aux_p, g.ldaux, i);
+                    for (int u = 0; u < RUNS; ++u) put(u, run(I, u) + bias[u]);
+                    drain(aux_p, g.ldaux, I);
                 }
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 x = xv(j, q) + bias[j][q];
-                        put(j, q, f32x4{act<EPI>(x[0]), act<EPI>(x[1]), act<EPI>(x[2]), act<EPI>(x[3])});
-                    }
-                drain(static_cast<__bf16 *>(Cbase), ldc, i);
+                for (int u = 0; u < RUNS; ++u) {
+                    const f32x4 x = run(I, u) + bias[u];
+                    put(u, f32x4{act<EPI>(x[0]), act<EPI>(x[1]), act<EPI>(x[2]), act<EPI>(x[3])});
+                }
+                drain(static_cast<__bf16 *>(Cbase), ldc, I);
             }
         }
     }
@@ -581,14 +693,18 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
     g.tiles_m = (int)((a.M + BM - 1) / BM);
     g.tiles_n = (int)((a.N + BNO - 1) / BNO);
     const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(NW * 64);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY, NTS>), grid, block, 0, s, g);
+    // K-contiguous operands (the forward) run on 16x16x32 MFMAs, the K-major
+    // layouts of the backward on 32x32x16 (their transpose reads are laid out
+    // for 32-row fragments)
+    constexpr int MF = LAY == 0 ? 16 : 32;
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY, NTS, MF>), grid, block, 0, s, g);
     return hipGetLastError();
 }
 
 template <int BM, int BN, int BK, int S, int NW, bool IL>
 hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
 {
-    constexpr bool gated_ok = Cfg<BM, BN, BK, S, NW>::TN % 2 == 0;
+    constexpr bool gated_ok = Cfg<BM, BN, BK, S, NW, 16>::TN % 2 == 0 && Cfg<BM, BN, BK, S, NW, 16>::WTN >= 64;
     // A launch whose fp32 output exceeds half the 256 MB last-level cache
     // (a row-parallel partial at 8192 tokens is 256 MiB) streams it out with
     // non-temporal stores: it cannot stay cached for its consumer anyway,
