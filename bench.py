@@ -837,6 +837,17 @@ def cpu_baseline(args, hl, dec):
     return cb, par
 
 
+def copy_scale(kib):
+    """Scale of a byte counter from its per-dispatch readings (KiB) for the
+    runtime's copy kernel: the three 1 GiB calibration copies are the large
+    readings; the runtime's own small copies in the same run (a few KiB) are
+    left out."""
+    big = [v for v in kib if v >= 0.25 * max(kib)]
+    if len(big) != 3:
+        raise ValueError("expected the three 1 GiB calibration copies, found %d large copies" % len(big))
+    return round(1048576.0 / (sum(big) / len(big)), 4)
+
+
 def write_traffic(prof_dir):
     """profiles/traffic.json from two rocprofv3 --pmc runs of the headline
     (FETCH_SIZE under <prof_dir>/pmcf, WRITE_SIZE under <prof_dir>/pmcw),
@@ -856,9 +867,8 @@ def write_traffic(prof_dir):
 
     F = load(os.path.join(prof_dir, "pmcf", "p_counter_collection.csv"))
     W = load(os.path.join(prof_dir, "pmcw", "p_counter_collection.csv"))
-    cal = "__amd_rocclr_copyBuffer"
-    sf = round(1048576.0 / (sum(F[cal]) / len(F[cal])), 4)   # counters are KiB per dispatch
-    sw = round(1048576.0 / (sum(W[cal]) / len(W[cal])), 4)
+    sf = copy_scale(F["__amd_rocclr_copyBuffer"])
+    sw = copy_scale(W["__amd_rocclr_copyBuffer"])
     M, H, Fs = 8192, 8192, 4096
     alg = {"gemm_up_gelu": 2 * (M * H + Fs * H + Fs) + 2 * M * Fs, "gemm_rowpar_partial": 2 * (M * Fs + H * Fs) + 4 * M * H}
     # the headline's two launches: 256x256 tiles, 8 waves, epilogue 0 (bias +

@@ -51,6 +51,15 @@ def test_stale_or_missing_traffic_record_reads_as_none(tmp_path, monkeypatch):
     assert bench.measured_traffic(key) is None
 
 
+def test_copy_calibration_uses_the_three_large_copies_only():
+    # readings (KiB per dispatch) of one counter run: three 1 GiB copies and
+    # a small copy made by the runtime; the small one must not dilute the scale
+    assert abs(bench.copy_scale([524308.4, 524299.5, 524299.5, 6.6]) - 2.0) < 1e-3
+    assert bench.copy_scale([1048576.0, 1048576.0, 1048576.0, 8.0]) == 1.0
+    with pytest.raises(ValueError):
+        bench.copy_scale([524308.4, 6.6])
+
+
 def test_cpu_model_is_a_string_or_none():
     m = bench.cpu_model()
     assert m is None or (isinstance(m, str) and m)
