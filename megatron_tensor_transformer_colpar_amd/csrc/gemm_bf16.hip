@@ -121,7 +121,7 @@ __device__ __forceinline__ void pin_rows16()
     }
 }
 
-template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY, bool NTS, int MF>
+template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY, bool NTS, int MF, bool DB>
 __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 {
     using C_ = Cfg<BM, BN, BK, S, NW, MF>;
@@ -138,11 +138,20 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     constexpr bool GATED = epi_gated(EPI);
     static_assert(!GATED || TN % 2 == 0, "gated tiles pair accumulator tiles within a wave");
     constexpr int BNO = GATED ? BN / 2 : BN;   // output columns per tile
-    __shared__ u32x4 st0[STAGE];
-    __shared__ u32x4 st1[STAGE];
-    __shared__ u32x4 st2[S > 2 ? STAGE : 1];
-    __shared__ u32x4 st3[S > 3 ? STAGE : 1];
-    __shared__ u32x4 st4[S > 4 ? STAGE : 1];
+    // LDS.  A stage holds one K slice of both tiles, A rows first.  With DB
+    // ("deep B") the two tiles have rings of their own: two A stages and
+    // three B stages, five arrays of 32 KiB (all 160 KiB of LDS for the
+    // 256 x 256 tile), so a B slice is requested two slices before its use
+    // instead of one; every stage is an array of its own, so the compiler
+    // never waits for the DMA of one stage before reading another.
+    static_assert(!DB || (MF == 16 && S == 2 && LAY == 0 && !epi_gated(EPI)), "deep-B ring shape");
+    constexpr int SZ01 = DB ? BM * CH : STAGE, SZB = DB ? BN * CH : STAGE;
+    constexpr int SB = DB ? 3 : S;   // B stages (A stages: S)
+    __shared__ u32x4 st0[SZ01];
+    __shared__ u32x4 st1[SZ01];
+    __shared__ u32x4 st2[DB || S > 2 ? SZB : 1];
+    __shared__ u32x4 st3[DB || S > 3 ? SZB : 1];
+    __shared__ u32x4 st4[DB || S > 4 ? SZB : 1];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -210,10 +219,13 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     // The row offset stays in the per-lane voffset, which the buffer range
     // check covers, so rows past M or N read zero; the in-row K offset goes
     // in soffset.  Refills past the last slice re-read the last slice.
-    // issue_part(stage, kt, lo, hi) issues DMA instructions lo .. hi-1 of a
-    // slice (the A_LD instructions of the A tile, then the B_LD of the B tile).
-    auto issue_part = [&](u32x4 *stage, int kt, int lo, int hi) __attribute__((always_inline)) {
-        const uint32_t koff = (uint32_t)min(kt, KT - 1) * (BK * 2);
+    // issue_part(sa, sb, kta, ktb, lo, hi) issues DMA instructions lo .. hi-1
+    // of a refill: the A_LD instructions of A slice kta into sa, then the B_LD
+    // of B slice ktb into sb (one slice of a shared stage: sb = sa + BM*CH).
+    auto issue_part = [&](u32x4 *sa, u32x4 *sb, int kta, int ktb, int lo, int hi) __attribute__((always_inline)) {
+        int kt = kta;
+        u32x4 *const stage = sa;
+        uint32_t koff = (uint32_t)min(kt, KT - 1) * (BK * 2);
 #pragma unroll
         for (int j = 0; j < C_::A_LD; ++j) {
             if (j < lo || j >= hi) continue;
@@ -224,29 +236,33 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(stage + (NW * j + wave) * 64), 16,
                                                         a_voff + j * a_jstep, koff, 0, 0);
         }
+        kt = ktb;
+        koff = (uint32_t)min(kt, KT - 1) * (BK * 2);
 #pragma unroll
         for (int j = 0; j < C_::B_LD; ++j) {
             if (C_::A_LD + j < lo || C_::A_LD + j >= hi) continue;
             if constexpr (BKM) {
                 const uint32_t vo = bk_voff + j * bk_jstep + (uint32_t)min(kt, KT - 1) * (uint32_t)(BK * g.ldb * 2);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16, vo,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(sb + (NW * j + wave) * 64), 16, vo,
                                                         0, 0, 0);
             } else if constexpr (GATED) {
                 // the offset goes through a local: an array element passed
                 // straight to the builtin also makes the host pass drop the stub
                 const uint32_t vo = gv_off[j];
                 if (gv_up[j])
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb2, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16,
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb2, LDS_PTR(sb + (NW * j + wave) * 64), 16,
                                                             vo, koff, 0, 0);
                 else
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16,
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(sb + (NW * j + wave) * 64), 16,
                                                             vo, koff, 0, 0);
             } else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(stage + BM * CH + (NW * j + wave) * 64), 16,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(sb + (NW * j + wave) * 64), 16,
                                                         b_voff + j * b_jstep, koff, 0, 0);
         }
     };
-    auto issue = [&](u32x4 *stage, int kt) __attribute__((always_inline)) { issue_part(stage, kt, 0, C_::LOADS); };
+    auto issue = [&](u32x4 *stage, int kt) __attribute__((always_inline)) {
+        issue_part(stage, stage + BM * CH, kt, kt, 0, C_::LOADS);
+    };
 
     // fragment geometry: lane reads row (lane % MF) of each MF-row tile,
     // K chunk CPQ*q + lane/MF of the slice (32x32x16: 16 k per step, lanes
@@ -389,8 +405,11 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     // DMA; sched_group_barriers pin that order.
     static_assert(MF == 32 || (KQ == 2 && TN <= TM && !AKM && !BKM), "16x16x32 main loop shape");
     constexpr int DPR = (C_::LOADS + TM - 1) / TM;   // refill DMA instructions per row
-    auto step16 = [&](auto refill_tag, const u32x4 *rstage, int rq, int pm, int pr, u32x4 *refill,
-                      int kt_refill) __attribute__((always_inline)) {
+    const int b_off = b_base - BM * CH;   // B fragment offset from the B tile
+    // step16 reads k-step rq of the A and B slices at ra, rb and (refill)
+    // issues A slice kta into fa_st and B slice ktb into fb_st
+    auto step16 = [&](auto refill_tag, const u32x4 *ra, const u32x4 *rb, int rq, int pm, int pr, u32x4 *fa_st,
+                      u32x4 *fb_st, int kta, int ktb) __attribute__((always_inline)) {
         constexpr bool RF = decltype(refill_tag)::value;
         if constexpr (MF == 16) {
             const int slot = (C_::CPQ * rq + fq) ^ fsw;
@@ -399,65 +418,97 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[pm][j], fa[0][i], acc[i][j], 0, 0, 0);
-                fa[0][i] = __builtin_bit_cast(bf16x8, rstage[a_base + i * MF * CH + slot]);
-                if (i < TN) fb[pr][i] = __builtin_bit_cast(bf16x8, rstage[b_base + i * MF * CH + slot]);
-                if constexpr (RF) issue_part(refill, kt_refill, i * DPR, min((i + 1) * DPR, C_::LOADS));
+                fa[0][i] = __builtin_bit_cast(bf16x8, ra[a_base + i * MF * CH + slot]);
+                if (i < TN) fb[pr][i] = __builtin_bit_cast(bf16x8, rb[b_off + i * MF * CH + slot]);
+                if constexpr (RF)
+                    issue_part(fa_st, fb_st, kta, ktb, i * DPR, min((i + 1) * DPR, C_::LOADS));
             }
             pin_rows16<0, TM, TN, DPR, C_::LOADS, RF>();
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // one K slice in `cur`: k-step 0 (reading k-step 1 of `cur`), the
-    // barrier that publishes `nxt`, k-step 1 (reading k-step 0 of `nxt`,
-    // refilling `cur` with slice kt + S)
-    auto slice16 = [&](u32x4 *cur, u32x4 *nxt, int kt) __attribute__((always_inline)) {
-        step16(std::false_type{}, cur, 1, 0, 1, cur, 0);
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 2) * C_::LOADS));
+    // One K slice, A in ca and B in cb: k-step 0 (reading k-step 1 of the
+    // slice), the barrier that publishes the next slice (na, nb), k-step 1
+    // (reading k-step 0 of the next slice, refilling ca with A slice kt + S
+    // and cb with B slice kt + SB).  The barrier's wait leaves in flight only
+    // what was requested after the next slice: with DB the B slice two ahead
+    // (each refill requests A before B, so the deeper ring's loads are the
+    // youngest).
+    constexpr int LOOP_WAIT = DB ? C_::B_LD : (S - 2) * C_::LOADS;
+    auto slice16 = [&](u32x4 *ca, u32x4 *cb, u32x4 *na, u32x4 *nb, int kt) __attribute__((always_inline)) {
+        step16(std::false_type{}, ca, cb, 1, 0, 1, ca, cb, 0, 0);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LOOP_WAIT));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        step16(std::true_type{}, nxt, 0, 1, 0, cur, kt + S);
+        step16(std::true_type{}, na, nb, 0, 1, 0, ca, cb, kt + S, kt + SB);
     };
 
     u32x4 *const ring[5] = {st0, st1, st2, st3, st4};
 
-    // prologue: slices 0 .. S-1 in flight, slice 0 landed and published
-#pragma unroll
-    for (int r = 0; r < S; ++r) issue(ring[r], r);
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 1) * C_::LOADS));
-    __builtin_amdgcn_s_barrier();
+    int kt = 0;
     if constexpr (MF == 16) {
+        // A stage r is ring[r]; B stage r the B part of ring[r], or with DB
+        // the array ring[2 + r]
+        u32x4 *ring_a[5], *ring_b[5];
+#pragma unroll
+        for (int r = 0; r < 5; ++r) {
+            ring_a[r] = ring[r];
+            ring_b[r] = DB ? ring[(2 + r) % 5] : r < S ? ring[r] + BM * CH : ring[r];
+        }
+        // prologue: A slices 0 .. S-1 and B slices 0 .. SB-1 in flight,
+        // slice 0 landed and published
+        constexpr int PRO = S > SB ? S : SB;
+#pragma unroll
+        for (int r = 0; r < PRO; ++r)
+            issue_part(ring_a[r], ring_b[r], r, r, r < S ? 0 : C_::A_LD, r < SB ? C_::LOADS : C_::A_LD);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(DB ? C_::LOADS + C_::B_LD : (S - 1) * C_::LOADS));
+        __builtin_amdgcn_s_barrier();
         // the first k-step's fragments, read in the order step16 reads them,
         // so that the waits the compiler places at the top of the main loop
         // (merged over its entry and its back edge) name the reads they need
         const int slot0 = fq ^ fsw;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            fa[0][i] = __builtin_bit_cast(bf16x8, st0[a_base + i * MF * CH + slot0]);
-            if (i < TN) fb[0][i] = __builtin_bit_cast(bf16x8, st0[b_base + i * MF * CH + slot0]);
+            fa[0][i] = __builtin_bit_cast(bf16x8, ring_a[0][a_base + i * MF * CH + slot0]);
+            if (i < TN) fb[0][i] = __builtin_bit_cast(bf16x8, ring_b[0][b_off + i * MF * CH + slot0]);
         }
         __builtin_amdgcn_sched_barrier(0);
+        // unrolled over a whole turn of both rings
+        constexpr int U = DB ? 6 : S;
+        for (; kt + U <= KT; kt += U) {
+#pragma unroll
+            for (int r = 0; r < U; ++r)
+                slice16(ring_a[r % S], ring_b[r % SB], ring_a[(r + 1) % S], ring_b[(r + 1) % SB], kt + r);
+        }
+        // the last KT % U slices, each reached only through the one before
+        // it, so the compiler's record of the DMA in flight stays exact (as a
+        // row of independent ifs its merged record made every fragment read
+        // wait for all loads in flight)
+        auto rest = [&](auto self, auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            if constexpr (r + 1 < U) {
+                if (kt + r < KT) {
+                    slice16(ring_a[r % S], ring_b[r % SB], ring_a[(r + 1) % S], ring_b[(r + 1) % SB], kt + r);
+                    self(self, std::integral_constant<int, r + 1>{});
+                }
+            }
+        };
+        rest(rest, std::integral_constant<int, 0>{});
     } else {
+        // prologue: slices 0 .. S-1 in flight, slice 0 landed and published
+#pragma unroll
+        for (int r = 0; r < S; ++r) issue(ring[r], r);
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 1) * C_::LOADS));
+        __builtin_amdgcn_s_barrier();
         read_frags(st0, 0, 0);
-    }
-
-    int kt = 0;
-    for (; kt + S <= KT; kt += S) {
+        for (; kt + S <= KT; kt += S) {
 #pragma unroll
-        for (int r = 0; r < S; ++r) {
-            if constexpr (MF == 16)
-                slice16(ring[r], ring[(r + 1) % S], kt + r);
-            else
-                slice(ring[r], ring[(r + 1) % S], kt + r);
+            for (int r = 0; r < S; ++r) slice(ring[r], ring[(r + 1) % S], kt + r);
         }
-    }
 #pragma unroll
-    for (int r = 0; r + 1 < S; ++r)
-        if (kt + r < KT) {
-            if constexpr (MF == 16)
-                slice16(ring[r], ring[r + 1], kt + r);
-            else
-                slice(ring[r], ring[r + 1], kt + r);
-        }
+        for (int r = 0; r + 1 < S; ++r)
+            if (kt + r < KT) slice(ring[r], ring[r + 1], kt + r);
+    }
     // drain the clamped refills before the workgroup exits
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
@@ -490,14 +541,16 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         return MF == 32 ? (lane >> 5) : ((lane >> 4) & 1);
     };
     const bool full = (m0 + BM <= g.M) && (n0 + BNO <= g.N);
-    // 4 bias values at column n (zeros past N or without a bias)
-    auto load_bias4 = [&](const __bf16 *bp, int n) __attribute__((always_inline)) {
-        f32x4 v = f32x4{};
-        if (bp && (full || n < g.N)) {
-            const bf16x4 b4 = *reinterpret_cast<const bf16x4 *>(bp + n);
-            v = f32x4{(float)b4[0], (float)b4[1], (float)b4[2], (float)b4[3]};
-        }
-        return v;
+    // 4 bias values at column n: zeros past N or without a bias (a resource
+    // of 0 bytes), through the buffer range check, so the loads of every run
+    // are issued together with no branch between them
+    auto bias_rsrc = [&](const __bf16 *bp) __attribute__((always_inline)) {
+        return make_rsrc(bp, bp ? (uint32_t)g.N * 2 : 0u);
+    };
+    auto load_bias4 = [&](__amdgpu_buffer_rsrc_t rbias, int n) __attribute__((always_inline)) {
+        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rbias, n * 2, 0, 0));
+        return f32x4{__builtin_bit_cast(float, w[0] << 16), __builtin_bit_cast(float, w[0] & 0xFFFF0000u),
+                     __builtin_bit_cast(float, w[1] << 16), __builtin_bit_cast(float, w[1] & 0xFFFF0000u)};
     };
     if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_ACC_F32) {
         // fp32 output leaves through LDS, one 32x32 block (a band's columns
@@ -512,7 +565,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         // LDS operations complete in issue order, so no wait separates its
         // writes from its reads or one block's reads from the next block's
         // writes.
-        static_assert(NW * 32 * 32 * 4 <= STAGE * 16, "epilogue staging area");
+        static_assert(NW * 32 * 32 * 4 <= SZ01 * 16, "epilogue staging area");
         __syncthreads();   // every wave is done reading the last slice
         float *const stg = reinterpret_cast<float *>(st0) + wave * 32 * 32;
         const int mw = m0 + wm * C_::WTM, nw = n0 + wn * C_::WTN;
@@ -557,7 +610,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         // of one instruction and the row-wise 16-byte reads spread over the
         // banks.
         constexpr int CPL = BNO / 8;   // 16-byte chunks per output row
-        static_assert(BM * BNO * 2 <= STAGE * 16, "gated staging area");
+        static_assert(BM * BNO * 2 <= SZ01 * 16, "gated staging area");
         static_assert((BM * CPL) % (64 * NW) == 0 && 64 % CPL == 0, "gated drain geometry");
         const __bf16 *const bias2_p = g.bias2[bt];
         __syncthreads();   // every wave is done reading the last slice
@@ -568,7 +621,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
             const int uu = MF == 32 ? u + RUNS / 2 : u + TN / 2;
             const int c = wn * (C_::WTN / 16) + run_chunk(u);
             const int n = n0 + 8 * c + 4 * run_half(u);
-            const f32x4 bgv = load_bias4(bias_p, n), buv = load_bias4(bias2_p, n);
+            const f32x4 bgv = load_bias4(bias_rsrc(bias_p), n), buv = load_bias4(bias_rsrc(bias2_p), n);
 #pragma unroll
             for (int I = 0; I < BANDS; ++I) {
                 const int r = wm * C_::WTM + 32 * I + run_row(u);
@@ -596,14 +649,14 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         // writes 64/CHR rows x CHR*16 contiguous bytes: whole 128-byte lines
         // when WTN = 64.
         constexpr int CHR = RUNS, RPI = 64 / CHR;
-        static_assert(NW * 32 * CHR <= STAGE, "epilogue staging area");
+        static_assert(NW * 32 * CHR <= SZ01, "epilogue staging area");
         __syncthreads();   // every wave is done reading the last slice
         u32x4 *const stg = st0 + wave * 32 * CHR;
         const int mw = m0 + wm * C_::WTM, nw = n0 + wn * C_::WTN;
         f32x4 bias[RUNS];
 #pragma unroll
         for (int u = 0; u < RUNS; ++u)
-            bias[u] = epi_has_bias(EPI) ? load_bias4(bias_p, nw + 8 * run_chunk(u) + 4 * run_half(u)) : f32x4{};
+            bias[u] = epi_has_bias(EPI) ? load_bias4(bias_rsrc(bias_p), nw + 8 * run_chunk(u) + 4 * run_half(u)) : f32x4{};
         auto put = [&](int u, f32x4 v) __attribute__((always_inline)) {
             const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
             const int r = run_row(u);
@@ -667,7 +720,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     }
 }
 
-template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY, bool NTS = false>
+template <int BM, int BN, int BK, int S, int NW, bool IL, int EPI, int LAY, bool NTS = false, bool DB = false>
 hipError_t launch_one(const GemmArgs &a, hipStream_t s)
 {
     GemmDev g;
@@ -697,7 +750,7 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
     // layouts of the backward on 32x32x16 (their transpose reads are laid out
     // for 32-row fragments)
     constexpr int MF = LAY == 0 ? 16 : 32;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY, NTS, MF>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY, NTS, MF, DB>), grid, block, 0, s, g);
     return hipGetLastError();
 }
 
@@ -714,6 +767,12 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
     // Smaller outputs, such as the 2048-token block's four partials (128 MiB)
     // that its reduce reads right after, stay cached.
     const bool stream = (int64_t)a.batch * a.M * a.N * 4 > (int64_t(128) << 20);
+    // The 256 x 256 forward tile takes a third B stage in the LDS it leaves
+    // free (the gated epilogue needs a 64 KiB staging area and keeps two
+    // shared stages).  A weight panel that is not in the last-level cache
+    // (the launch before streamed other operands through it) then has two
+    // slices to arrive instead of one.
+    constexpr bool DBC = BM == 256 && BN == 256 && BK == 64 && S == 2;
     if (a.layout == LAYOUT_B_KMAJOR) {   // input gradients
         switch (epi) {
         case EPI_STORE_F32:
@@ -733,12 +792,12 @@ hipError_t launch_cfg(const GemmArgs &a, Epilogue epi, hipStream_t s)
         }
     }
     switch (epi) {
-    case EPI_BIAS_GELU: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU, 0>(a, s);
+    case EPI_BIAS_GELU: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU, 0, false, DBC>(a, s);
     case EPI_STORE_F32:
-        return stream ? launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 0, true>(a, s)
-                      : launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 0>(a, s);
-    case EPI_BIAS_GELU_ERF: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU_ERF, 0>(a, s);
-    case EPI_BIAS: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS, 0>(a, s);
+        return stream ? launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 0, true, DBC>(a, s)
+                      : launch_one<BM, BN, BK, S, NW, IL, EPI_STORE_F32, 0, false, DBC>(a, s);
+    case EPI_BIAS_GELU_ERF: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS_GELU_ERF, 0, false, DBC>(a, s);
+    case EPI_BIAS: return launch_one<BM, BN, BK, S, NW, IL, EPI_BIAS, 0, false, DBC>(a, s);
     case EPI_GATED_TANH:
         if constexpr (gated_ok) return launch_one<BM, BN, BK, S, NW, IL, EPI_GATED_TANH, 0>(a, s);
         break;
