@@ -114,4 +114,21 @@ __device__ __forceinline__ void map_tile(int bid, int batch, int tiles_m, int ti
     tn = r / gsize;
 }
 
+// Workgroup id -> (tile_m, tile_n) for one problem whose tile columns split
+// evenly over the 8 XCDs: XCD x owns columns [x W, (x+1) W), W = tiles_n / 8,
+// and walks them in groups of 8 tile rows.  Each round of the XCD's workgroups
+// still covers an 8 x W block (the L2 reuse of map_tile), but the B panels of
+// an XCD stay the same from round to round, so the first round touches every
+// B panel of the problem and later rounds find them in the last-level cache
+// instead of fetching new ones from HBM at every tile start.
+__device__ __forceinline__ void map_tile_bands(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int x = bid & 7, l = bid >> 3, W = tiles_n >> 3;
+    const int group = l / (8 * W), r = l - group * 8 * W;
+    const int first_m = group * 8;
+    const int gsize = min(tiles_m - first_m, 8);
+    tm = first_m + r % gsize;
+    tn = x * W + r / gsize;
+}
+
 }  // namespace tpk

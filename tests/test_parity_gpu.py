@@ -166,6 +166,34 @@ def test_ragged_tokens_on_the_largest_tile(train, M, H, Fs):
         assert eu <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("M", [1800, 2600, 8192])
+def test_rowpar_band_order_every_tile(M):
+    # the row-parallel launch at H = 8192 on the 256 x 256 tile (32 tile
+    # columns, four per XCD) takes the band tile order; 1800 tokens make one
+    # group of 8 tile rows whose last is partial, 2600 a full group of 8 and
+    # a group of 3.  One token row
+    # per tile row and tile column pair (row r = 256 tm + (37 tm) % 256, every
+    # column) is checked, so a tile the order skipped or computed twice fails
+    H, Fs = 8192, 512
+    w = inputs.Workload(44, "rowpar_bands", "bf16", M=M, H=H, F=Fs, T=1)
+    X, W1, b1, W2 = inputs.mlp_inputs(w)
+    dev = DeviceMLP(X, W1, b1, W2)
+    Z = torch.full((M, H), float("nan"), dtype=torch.float32, device="cuda")
+    Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+    tp.tp_colpar_gelu(dev.X, dev.W1t, dev.b1, Y, M, H, Fs, 1, 0, tp.TP_BF16)
+    tp.tp_rowpar_partial(Y, dev.W2t, Z, M, H, Fs, 1, 0, tp.TP_BF16)
+    torch.cuda.synchronize()
+    assert not torch.isnan(Z).any()
+    tiles_m = (M + 255) // 256
+    rows = np.array(sorted({min(M - 1, 256 * tm + (37 * tm) % 256) for tm in range(tiles_m)}))
+    _, Zr = oracle.mlp_shard(X.f64[rows], W1.f64, b1.f64, W2.f64, 1, 0)
+    Zg = to_f64(Z)[rows]
+    for tn in range(H // 256):
+        cols = slice(256 * tn, 256 * tn + 256)
+        e = rel_fro(Zg[:, cols], Zr[:, cols])
+        assert e <= TOL["bf16"], (tn, e)
+
+
 def test_full_matrix_and_rank_local_calls_agree_bitwise():
     # Shard i of the full W1^T/W2^T (F, T, i) is the same computation as the
     # stand-alone shard matrices (F/T, 1, 0); first and last shard.
