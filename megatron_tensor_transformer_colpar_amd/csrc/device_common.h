@@ -114,16 +114,21 @@ __device__ __forceinline__ void map_tile(int bid, int batch, int tiles_m, int ti
     tn = r / gsize;
 }
 
-// Workgroup id -> (tile_m, tile_n) for one problem whose tile columns split
-// evenly over the 8 XCDs: XCD x owns columns [x W, (x+1) W), W = tiles_n / 8,
-// and walks them in groups of 8 tile rows.  Each round of the XCD's workgroups
-// still covers an 8 x W block (the L2 reuse of map_tile), but the B panels of
-// an XCD stay the same from round to round, so the first round touches every
-// B panel of the problem and later rounds find them in the last-level cache
-// instead of fetching new ones from HBM at every tile start.
-__device__ __forceinline__ void map_tile_bands(int bid, int tiles_m, int tiles_n, int &tm, int &tn)
+// Workgroup id -> (batch entry, tile_m, tile_n) for problems whose tile
+// columns split evenly over the 8 XCDs: XCD x owns columns [x W, (x+1) W)
+// of every batch entry, W = tiles_n / 8, and walks them entry by entry in
+// groups of 8 tile rows.  Each round of an XCD's workgroups still covers an
+// 8 x W block (the L2 reuse of map_tile), but every XCD works on the same
+// entry at a time and keeps its B panels from round to round: the first
+// round of an entry touches each of its B panels once and the later rounds
+// find them in the last-level cache, instead of fetching new panels from
+// HBM at every tile start.
+__device__ __forceinline__ void map_tile_bands(int bid, int tiles_m, int tiles_n, int &bt, int &tm, int &tn)
 {
-    const int x = bid & 7, l = bid >> 3, W = tiles_n >> 3;
+    const int x = bid & 7, W = tiles_n >> 3, per_entry = tiles_m * W;
+    int l = bid >> 3;
+    bt = l / per_entry;
+    l -= bt * per_entry;
     const int group = l / (8 * W), r = l - group * 8 * W;
     const int first_m = group * 8;
     const int gsize = min(tiles_m - first_m, 8);

@@ -48,7 +48,7 @@ struct GemmDev {
     int64_t ldc[kMaxBatch];
     int M, N, K;
     int tiles_m, tiles_n, batch;
-    int bands;   // tile order of map_tile_bands (one problem, W = tiles_n / 8 columns per XCD)
+    int bands;   // tile order of map_tile_bands (W = tiles_n / 8 columns per XCD)
 };
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
@@ -162,8 +162,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 
     int bt, tile_m, tile_n;
     if (g.bands) {
-        bt = 0;
-        map_tile_bands(blockIdx.x, g.tiles_m, g.tiles_n, tile_m, tile_n);
+        map_tile_bands(blockIdx.x, g.tiles_m, g.tiles_n, bt, tile_m, tile_n);
     } else {
         map_tile<8>(blockIdx.x, g.batch, g.tiles_m, g.tiles_n, bt, tile_m, tile_n);
     }
@@ -751,12 +750,12 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
     constexpr int BNO = epi_gated(EPI) ? BN / 2 : BN;
     g.tiles_m = (int)((a.M + BM - 1) / BM);
     g.tiles_n = (int)((a.N + BNO - 1) / BNO);
-    // Row-parallel partials of one problem on the 256 x 256 tile with at
-    // least 4 tile columns per XCD take the band order: alternating with the column-parallel launch at
-    // the prefill shape (whose operands push W2 out of the last-level cache),
-    // the pair took 770.3 instead of 785.3 us, bit-identical.
-    g.bands = EPI == EPI_STORE_F32 && LAY == 0 && BM == 256 && BN == 256 && g.batch == 1 && g.tiles_n % 8 == 0 &&
-              g.tiles_n >= 32;
+    // Row-parallel partials on the 256 x 256 tile with at least 4 tile
+    // columns per XCD take the band order: alternating with the column-
+    // parallel launch at the prefill shape (whose operands push W2 out of
+    // the last-level cache), the pair took 770.3 instead of 785.3 us,
+    // bit-identical.
+    g.bands = EPI == EPI_STORE_F32 && LAY == 0 && BM == 256 && BN == 256 && g.tiles_n % 8 == 0 && g.tiles_n >= 32;
     const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(NW * 64);
     // K-contiguous operands (the forward) run on 16x16x32 MFMAs, the K-major
     // layouts of the backward on 32x32x16 (their transpose reads are laid out
