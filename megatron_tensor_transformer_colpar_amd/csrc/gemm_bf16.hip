@@ -145,7 +145,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     // 256 x 256 tile), so a B slice is requested two slices before its use
     // instead of one; every stage is an array of its own, so the compiler
     // never waits for the DMA of one stage before reading another.
-    static_assert(!DB || (MF == 16 && S == 2 && LAY == 0 && !epi_gated(EPI)), "deep-B ring shape");
+    static_assert(!DB || (S == 2 && !epi_gated(EPI)), "deep-B ring shape");
     constexpr int SZ01 = DB ? BM * CH : STAGE, SZB = DB ? BN * CH : STAGE;
     constexpr int SB = DB ? 3 : S;   // B stages (A stages: S)
     __shared__ u32x4 st0[SZ01];
@@ -265,9 +265,6 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
                                                         b_voff + j * b_jstep, koff, 0, 0);
         }
     };
-    auto issue = [&](u32x4 *stage, int kt) __attribute__((always_inline)) {
-        issue_part(stage, stage + BM * CH, kt, kt, 0, C_::LOADS);
-    };
 
     // fragment geometry: lane reads row (lane % MF) of each MF-row tile,
     // K chunk CPQ*q + lane/MF of the slice (32x32x16: 16 k per step, lanes
@@ -304,21 +301,23 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     };
 
     bf16x8 fa[2][TM], fb[2][TN];
-    auto read_frags = [&](const u32x4 *stage, int q, int p) __attribute__((always_inline)) {
+    const int b_off = b_base - BM * CH;   // B fragment offset from the B tile
+    // the fragments of k-step q of the A slice at sa and the B slice at sb
+    auto read_frags = [&](const u32x4 *sa, const u32x4 *sb, int q, int p) __attribute__((always_inline)) {
         const int slot = (C_::CPQ * q + fq) ^ fsw;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if constexpr (AKM)
-                fa[p][i] = tr_frag(stage, BM * 2, a_tr[i], q);
+                fa[p][i] = tr_frag(sa, BM * 2, a_tr[i], q);
             else
-                fa[p][i] = __builtin_bit_cast(bf16x8, stage[a_base + i * MF * CH + slot]);
+                fa[p][i] = __builtin_bit_cast(bf16x8, sa[a_base + i * MF * CH + slot]);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             if constexpr (BKM)
-                fb[p][j] = tr_frag(stage + BM * CH, BN * 2, b_tr[j], q);
+                fb[p][j] = tr_frag(sb, BN * 2, b_tr[j], q);
             else
-                fb[p][j] = __builtin_bit_cast(bf16x8, stage[b_base + j * MF * CH + slot]);
+                fb[p][j] = __builtin_bit_cast(bf16x8, sb[b_off + j * MF * CH + slot]);
         }
     };
 
@@ -367,16 +366,16 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
             __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
         }
     };
-    auto phase = [&](const u32x4 *stage, int q, int p_read, int p_mfma) __attribute__((always_inline)) {
-        read_frags(stage, q, p_read);
+    auto phase = [&](const u32x4 *sa, const u32x4 *sb, int q, int p_read, int p_mfma) __attribute__((always_inline)) {
+        read_frags(sa, sb, q, p_read);
         mfmas(p_mfma);
         pin_reads();
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto phase_refill = [&](u32x4 *refill, int kt_refill, const u32x4 *stage, int p_read,
+    auto phase_refill = [&](u32x4 *ra, u32x4 *rb, int kta, int ktb, const u32x4 *sa, const u32x4 *sb, int p_read,
                             int p_mfma) __attribute__((always_inline)) {
-        read_frags(stage, 0, p_read);
-        issue(refill, kt_refill);
+        read_frags(sa, sb, 0, p_read);
+        issue_part(ra, rb, kta, ktb, 0, C_::LOADS);
         mfmas(p_mfma);
         __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
 #pragma unroll
@@ -388,17 +387,22 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // One K slice held in `cur`; `nxt` holds the next slice (its DMA may
-    // still be in flight), and `cur` is refilled with slice kt + S.
-    auto slice = [&](u32x4 *cur, u32x4 *nxt, int kt) __attribute__((always_inline)) {
+    // The barrier's wait in every K slice leaves in flight only what was
+    // requested after the next slice: with DB the B slice two ahead (each
+    // refill requests A before B, so the deeper ring's loads are the
+    // youngest), else the S-2 younger slices.
+    constexpr int LOOP_WAIT = DB ? C_::B_LD : (S - 2) * C_::LOADS;
+    // One K slice, A in ca and B in cb; (na, nb) hold the next slice (its DMA
+    // may still be in flight); ca and cb are refilled with A slice kt + S and
+    // B slice kt + SB.
+    auto slice = [&](u32x4 *ca, u32x4 *cb, const u32x4 *na, const u32x4 *nb, int kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 1; q < KQ; ++q) phase(cur, q, q & 1, (q - 1) & 1);
-        // slice kt+1 landed (at most the S-2 younger slices still in
-        // flight) and every wave is done reading `cur`
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 2) * C_::LOADS));
+        for (int q = 1; q < KQ; ++q) phase(ca, cb, q, q & 1, (q - 1) & 1);
+        // the next slice landed and every wave is done reading this one
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LOOP_WAIT));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        phase_refill(cur, kt + S, nxt, 0, (KQ - 1) & 1);
+        phase_refill(ca, cb, kt + S, kt + SB, na, nb, 0, (KQ - 1) & 1);
     };
 
     // 16x16x32 tiles: a wave's fragments of both buffers would not fit
@@ -410,7 +414,6 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     // DMA; sched_group_barriers pin that order.
     static_assert(MF == 32 || (KQ == 2 && TN <= TM && !AKM && !BKM), "16x16x32 main loop shape");
     constexpr int DPR = (C_::LOADS + TM - 1) / TM;   // refill DMA instructions per row
-    const int b_off = b_base - BM * CH;   // B fragment offset from the B tile
     // step16 reads k-step rq of the A and B slices at ra, rb and (refill)
     // issues A slice kta into fa_st and B slice ktb into fb_st
     auto step16 = [&](auto refill_tag, const u32x4 *ra, const u32x4 *rb, int rq, int pm, int pr, u32x4 *fa_st,
@@ -435,11 +438,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     // One K slice, A in ca and B in cb: k-step 0 (reading k-step 1 of the
     // slice), the barrier that publishes the next slice (na, nb), k-step 1
     // (reading k-step 0 of the next slice, refilling ca with A slice kt + S
-    // and cb with B slice kt + SB).  The barrier's wait leaves in flight only
-    // what was requested after the next slice: with DB the B slice two ahead
-    // (each refill requests A before B, so the deeper ring's loads are the
-    // youngest).
-    constexpr int LOOP_WAIT = DB ? C_::B_LD : (S - 2) * C_::LOADS;
+    // and cb with B slice kt + SB).
     auto slice16 = [&](u32x4 *ca, u32x4 *cb, u32x4 *na, u32x4 *nb, int kt) __attribute__((always_inline)) {
         step16(std::false_type{}, ca, cb, 1, 0, 1, ca, cb, 0, 0);
         __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LOOP_WAIT));
@@ -450,24 +449,23 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 
     u32x4 *const ring[5] = {st0, st1, st2, st3, st4};
 
-    int kt = 0;
+    // A stage r is ring[r]; B stage r the B part of ring[r], or with DB the
+    // array ring[2 + r]
+    u32x4 *ring_a[5], *ring_b[5];
+#pragma unroll
+    for (int r = 0; r < 5; ++r) {
+        ring_a[r] = ring[r];
+        ring_b[r] = DB ? ring[(2 + r) % 5] : r < S ? ring[r] + BM * CH : ring[r];
+    }
+    // prologue: A slices 0 .. S-1 and B slices 0 .. SB-1 in flight, slice 0
+    // landed and published
+    constexpr int PRO = S > SB ? S : SB;
+#pragma unroll
+    for (int r = 0; r < PRO; ++r)
+        issue_part(ring_a[r], ring_b[r], r, r, r < S ? 0 : C_::A_LD, r < SB ? C_::LOADS : C_::A_LD);
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(DB ? C_::LOADS + C_::B_LD : (S - 1) * C_::LOADS));
+    __builtin_amdgcn_s_barrier();
     if constexpr (MF == 16) {
-        // A stage r is ring[r]; B stage r the B part of ring[r], or with DB
-        // the array ring[2 + r]
-        u32x4 *ring_a[5], *ring_b[5];
-#pragma unroll
-        for (int r = 0; r < 5; ++r) {
-            ring_a[r] = ring[r];
-            ring_b[r] = DB ? ring[(2 + r) % 5] : r < S ? ring[r] + BM * CH : ring[r];
-        }
-        // prologue: A slices 0 .. S-1 and B slices 0 .. SB-1 in flight,
-        // slice 0 landed and published
-        constexpr int PRO = S > SB ? S : SB;
-#pragma unroll
-        for (int r = 0; r < PRO; ++r)
-            issue_part(ring_a[r], ring_b[r], r, r, r < S ? 0 : C_::A_LD, r < SB ? C_::LOADS : C_::A_LD);
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(DB ? C_::LOADS + C_::B_LD : (S - 1) * C_::LOADS));
-        __builtin_amdgcn_s_barrier();
         // the first k-step's fragments, read in the order step16 reads them,
         // so that the waits the compiler places at the top of the main loop
         // (merged over its entry and its back edge) name the reads they need
@@ -478,42 +476,36 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
             if (i < TN) fb[0][i] = __builtin_bit_cast(bf16x8, ring_b[0][b_off + i * MF * CH + slot0]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // unrolled over a whole turn of both rings
-        constexpr int U = DB ? 6 : S;
-        for (; kt + U <= KT; kt += U) {
-#pragma unroll
-            for (int r = 0; r < U; ++r)
-                slice16(ring_a[r % S], ring_b[r % SB], ring_a[(r + 1) % S], ring_b[(r + 1) % SB], kt + r);
-        }
-        // the last KT % U slices, each reached only through the one before
-        // it, so the compiler's record of the DMA in flight stays exact (as a
-        // row of independent ifs its merged record made every fragment read
-        // wait for all loads in flight)
-        auto rest = [&](auto self, auto rc) __attribute__((always_inline)) {
-            constexpr int r = decltype(rc)::value;
-            if constexpr (r + 1 < U) {
-                if (kt + r < KT) {
-                    slice16(ring_a[r % S], ring_b[r % SB], ring_a[(r + 1) % S], ring_b[(r + 1) % SB], kt + r);
-                    self(self, std::integral_constant<int, r + 1>{});
-                }
-            }
-        };
-        rest(rest, std::integral_constant<int, 0>{});
     } else {
-        // prologue: slices 0 .. S-1 in flight, slice 0 landed and published
-#pragma unroll
-        for (int r = 0; r < S; ++r) issue(ring[r], r);
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((S - 1) * C_::LOADS));
-        __builtin_amdgcn_s_barrier();
-        read_frags(st0, 0, 0);
-        for (; kt + S <= KT; kt += S) {
-#pragma unroll
-            for (int r = 0; r < S; ++r) slice(ring[r], ring[(r + 1) % S], kt + r);
-        }
-#pragma unroll
-        for (int r = 0; r + 1 < S; ++r)
-            if (kt + r < KT) slice(ring[r], ring[r + 1], kt + r);
+        read_frags(ring_a[0], ring_b[0], 0, 0);
     }
+    auto one = [&](int r, int k) __attribute__((always_inline)) {
+        if constexpr (MF == 16)
+            slice16(ring_a[r % S], ring_b[r % SB], ring_a[(r + 1) % S], ring_b[(r + 1) % SB], k);
+        else
+            slice(ring_a[r % S], ring_b[r % SB], ring_a[(r + 1) % S], ring_b[(r + 1) % SB], k);
+    };
+    // unrolled over a whole turn of both rings
+    constexpr int U = DB ? 6 : S;
+    int kt = 0;
+    for (; kt + U <= KT; kt += U) {
+#pragma unroll
+        for (int r = 0; r < U; ++r) one(r, kt + r);
+    }
+    // the last KT % U slices, each reached only through the one before it,
+    // so the compiler's record of the DMA in flight stays exact (as a row of
+    // independent ifs its merged record made every fragment read wait for
+    // all loads in flight)
+    auto rest = [&](auto self, auto rc) __attribute__((always_inline)) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr (r + 1 < U) {
+            if (kt + r < KT) {
+                one(r, kt + r);
+                self(self, std::integral_constant<int, r + 1>{});
+            }
+        }
+    };
+    rest(rest, std::integral_constant<int, 0>{});
     // drain the clamped refills before the workgroup exits
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
 
