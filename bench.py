@@ -774,13 +774,14 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(args, hl, dec):
+def cpu_baseline(args, hl, dec, stack=False):
     """The fp64 oracle on the host cores, timed on bounded samples of the
     bench's own inputs, and the GPU outputs of those inputs checked against
     it.  Prefill: a seeded sample of the headline's token rows, sized to take
     about --cpu-seconds (no step of the block mixes rows, so the time
     extrapolates linearly to all rows; labelled).  Decode: the whole M = 32
-    step (MLP shard + out-projection shard)."""
+    step (MLP shard + out-projection shard).  With `stack`, one layer of the
+    80-layer stack as well (cpu_stack80)."""
     import numpy as np
 
     import oracle
@@ -834,7 +835,56 @@ def cpu_baseline(args, hl, dec):
         par["decode"] = {"rel_fro": errs, "tol": 5e-3,
                          "ok": all(v <= 5e-3 for e in errs.values() for v in e.values())}
         log("[bench] cpu oracle, decode: %.2fs, parity %s" % (dtd, errs))
+    if stack:
+        cb["stack80"] = cpu_stack80()
     return cb, par
+
+
+def cpu_stack80():
+    """The fp64 oracle on one layer of the 80-layer stack (H=8192, F=32768,
+    A=8192, T=8, the whole TP group: out-projection partials, reduce with
+    residual and RMS copy, MLP partials, reduce), on layer 0's seeded host
+    weights: the decode layer at M=8 in full, and a 32-row sample of the
+    prefill layer at M=4096.  Every layer has the same shape and no step of a
+    layer mixes token rows, so the step times extrapolate linearly to 80
+    layers and to all rows (labelled)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    from megatron_tensor_transformer_colpar_amd import inputs
+
+    w = inputs.WORKLOADS["stack80"]
+    H, F, A, T, L = w.H, w.F, w.A, w.T, w.layers
+    As = A // T
+    kw = dict(workload=w.wid, layer=0)
+    jobs = {"Wo": ((A, H), w.w_std, inputs.WO_ID), "W1": ((H, F), w.w_std, inputs.W1_ID),
+            "b1": ((F,), w.b_std, inputs.B1_ID), "W2": ((F, H), w.w_std, inputs.W2_ID)}
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        futs = {k: ex.submit(inputs.normal, shape, std, "bf16", tensor=tid, **kw) for k, (shape, std, tid) in jobs.items()}
+        wt = {k: f.result().f64 for k, f in futs.items()}     # converted to fp64 once, outside the timing
+    out = {}
+    flops_row = 2.0 * A * H + 4.0 * H * F            # the whole group's GEMM flops per token row
+    wbytes = 2.0 * (H * A + 2 * F * H + F)            # the layer's bf16 weights
+    for label, M, rows in (("decode", 8, 8), ("prefill", 4096, 32)):
+        h = inputs.normal((rows, H), 1.0, "f32", tensor=inputs.X_ID, **kw).f64
+        ctx = [inputs.normal((rows, As), 1.0, "bf16", tensor=inputs.CTX_ID, shard=i + 1, **kw).f64 for i in range(T)]
+        t0 = time.perf_counter()
+        oracle.layer_fwd(h, ctx, wt["Wo"], wt["W1"], wt["b1"], wt["W2"], T, 1e-6)
+        dt = time.perf_counter() - t0
+        step_s = dt * (M / rows) * L
+        e = {"layer_seconds": round(dt, 3), "rows": rows, "M": M, "cores": oracle.max_threads(),
+             "extrapolated_step_s_group": round(step_s, 2), "extrapolated_step_s_per_rank_share": round(step_s / T, 2),
+             "tflops": round(rows * flops_row / dt / 1e12, 5)}
+        if label == "decode":
+            e["weight_gbs"] = round(L * wbytes / step_s / 1e9, 3)
+            e["sample"] = "one layer of the whole TP group at M=8 (every row), fp64; x 80 layers extrapolated"
+        else:
+            e["sample"] = "32 of 4096 token rows of one layer of the whole TP group, fp64; x 4096/32 rows x 80 layers extrapolated"
+        out[label] = e
+        log("[bench] cpu oracle, stack80 %s: %s" % (label, e))
+    return out
 
 
 def copy_scale(kib):
@@ -991,7 +1041,7 @@ def main():
     if "context" in sections:
         rec["hipblaslt_context"] = hipblaslt_context(args, torch, tp)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, hl, dec_host)
+        rec["cpu_baseline"], rec["parity"] = cpu_baseline(args, hl, dec_host, stack="stack80" in sections)
     print(json.dumps(rec), flush=True)
 
 
