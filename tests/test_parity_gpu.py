@@ -194,6 +194,33 @@ def test_rowpar_band_order_every_tile(M):
         assert e <= TOL["bf16"], (tn, e)
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 320, 448, 704])
+def test_short_k_on_the_deep_b_ring(K):
+    # the 256 x 256 forward tile keeps two A and three B stages and unrolls
+    # six K slices; K = 64 .. 704 gives 1, 2, 3, 5, 7 and 11 slices, i.e.
+    # prologues whose refills re-read the last slice and remainders of 1 to 5
+    # slices after the unrolled loop.  Both launches run that tile here
+    # (4096 x 4096 outputs: 256 tiles), the column-parallel one with K = H
+    # and the row-parallel one with K = F/T.
+    M, N = 4096, 4096
+    wu = inputs.Workload(45, "short_k_up", "bf16", M=M, H=K, F=N, T=1)
+    X, W1, b1, _ = inputs.mlp_inputs(wu)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    tp.tp_colpar_gelu(X.torch(), W1.transposed().torch(), b1.torch(), Y, M, K, N, 1, 0, tp.TP_BF16)
+    wd = inputs.Workload(46, "short_k_down", "bf16", M=M, H=N, F=K, T=1)
+    Xd, _, _, W2 = inputs.mlp_inputs(wd)
+    Yd = inputs.normal((M, K), 1.0, "bf16", workload=46, tensor=inputs.X_ID + 20)
+    Z = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    tp.tp_rowpar_partial(Yd.torch(), W2.transposed().torch(), Z, M, N, K, 1, 0, tp.TP_BF16)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, 255, 256, 1000, 2047, 4095}))
+    Yr = oracle.colpar_gelu(X.f64[rows], W1.f64, b1.f64, 1, 0)
+    Zr = oracle.rowpar_partial(Yd.f64[rows], W2.f64, 1, 0)
+    ey, ez = rel_fro(to_f64(Y)[rows], Yr), rel_fro(to_f64(Z)[rows], Zr)
+    print("  K=%d: Y %.2e  Z %.2e" % (K, ey, ez))
+    assert ey <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
 def test_full_matrix_and_rank_local_calls_agree_bitwise():
     # Shard i of the full W1^T/W2^T (F, T, i) is the same computation as the
     # stand-alone shard matrices (F/T, 1, 0); first and last shard.
