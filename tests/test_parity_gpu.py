@@ -387,6 +387,29 @@ def test_reduce_bf16_copy_is_round_to_nearest_even():
     assert np.array_equal(ob.cpu().view(torch.int16).numpy().view(np.uint16), inputs.f32_to_bf16_bits(host))
 
 
+def test_reduce_bf16_copy_ties_subnormals_and_specials():
+    # one partial (the sum is the value itself): exact ties between two bf16
+    # neighbours go to the even one, subnormals round like normals, infinities
+    # stay, NaNs stay NaN; the device's conversion against the host RNE
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x00008000, 0x00018000, 0x7F7F8000, 0x7F7FFFFF],
+                    dtype=np.uint32).view(np.float32)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 1e-40, -1e-40, 3.4e38, -3.4e38, 1.5e-45], dtype=np.float32)
+    vals = np.concatenate([ties, special])
+    M, H = 2, 64
+    x = np.zeros((M, H), dtype=np.float32)
+    x.flat[:len(vals)] = vals
+    x[1, :] = np.nan
+    P = torch.from_numpy(x).cuda()
+    out = torch.empty(M, H, device="cuda")
+    ob = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    tp.tp_shard_reduce([P], 1, None, out, ob, M, H)
+    torch.cuda.synchronize()
+    got = ob.cpu().view(torch.int16).numpy().view(np.uint16)
+    want = inputs.f32_to_bf16_bits(x)
+    assert np.array_equal(got[0], want[0]), [hex(v) for v in got[0][:len(vals)]]
+    assert np.isnan(inputs.bf16_bits_to_f32(got[1])).all()
+
+
 # the row-RMS kernel runs 1024 threads per row, two 16-byte elements per
 # thread and pass: H = 64 leaves most threads idle, 4160 gives a ragged second
 # element, 8192 is exactly one pass, 12288 two passes; in place is how the
