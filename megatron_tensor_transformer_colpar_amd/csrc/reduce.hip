@@ -8,6 +8,12 @@
 // T loads of a step are issued before the adds.  The row-normalised variant
 // runs one workgroup per row and reduces the sum of squares with wavefront
 // shuffles, then across the sixteen waves through LDS.
+// Partials larger than half the 256 MB last-level cache are read with
+// non-temporal loads: they cannot stay cached anyway, and at the 80-layer
+// stack's prefill shape (eight 128 MiB partials and the residual, in place)
+// the plain reduce took 214 instead of 258 us with them (6.3 against 5.2
+// TB/s); partials the cache does hold (the 2048-token block's four) are
+// read faster through it.
 #include "device_common.h"
 #include "tp_kernels.h"
 
@@ -24,25 +30,34 @@ __device__ __forceinline__ u32x2 pack_bf16x4(f32x4 v)
     return __builtin_bit_cast(u32x2, b);
 }
 
-template <int T>
+template <bool STREAM>
+__device__ __forceinline__ f32x4 load_part(const f32x4 *p)
+{
+    if constexpr (STREAM)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+
+template <int T, bool STREAM>
 __device__ __forceinline__ f32x4 sum_partials(const PartialPtrs &P, int64_t i)
 {
     f32x4 v[T];
 #pragma unroll
-    for (int j = 0; j < T; ++j) v[j] = P.p[j][i];
+    for (int j = 0; j < T; ++j) v[j] = load_part<STREAM>(P.p[j] + i);
     f32x4 s = v[0];
 #pragma unroll
     for (int j = 1; j < T; ++j) s += v[j];
     return s;
 }
 
-template <int T>
+template <int T, bool STREAM>
 __global__ void __launch_bounds__(256) reduce_kernel(PartialPtrs P, const f32x4 *residual, f32x4 *out,
                                                      u32x2 *out_bf16, int64_t n4)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        f32x4 s = sum_partials<T>(P, i);
+        f32x4 s = sum_partials<T, STREAM>(P, i);
         if (residual) s = residual[i] + s;
         out[i] = s;
         if (out_bf16) out_bf16[i] = pack_bf16x4(s);
@@ -58,7 +73,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(PartialPtrs P, const f32x4 
 // 256 threads and one element per pass, 5.9 us like this).
 constexpr int RMS_THREADS = 1024;
 
-template <int T>
+template <int T, bool STREAM>
 __global__ void __launch_bounds__(RMS_THREADS) reduce_rms_kernel(PartialPtrs P, const f32x4 *residual, f32x4 *out,
                                                                  u32x2 *out_bf16, int64_t h4, float inv_h, float eps)
 {
@@ -74,8 +89,8 @@ __global__ void __launch_bounds__(RMS_THREADS) reduce_rms_kernel(PartialPtrs P, 
         f32x4 v[2][T + 1];
 #pragma unroll
         for (int j = 0; j < T; ++j) {
-            v[0][j] = P.p[j][base + c];
-            v[1][j] = P.p[j][base + c2];
+            v[0][j] = load_part<STREAM>(P.p[j] + base + c);
+            v[1][j] = load_part<STREAM>(P.p[j] + base + c2);
         }
         if (residual) {
             v[0][T] = residual[base + c];
@@ -118,13 +133,22 @@ hipError_t launch_t(const PartialPtrs &P, const float *residual, float *out, voi
     const f32x4 *r4 = reinterpret_cast<const f32x4 *>(residual);
     f32x4 *o4 = reinterpret_cast<f32x4 *>(out);
     u32x2 *b4 = static_cast<u32x2 *>(ob);
+    const bool stream = (int64_t)T * M * H * 4 > (int64_t(128) << 20);
     if (rms) {
-        hipLaunchKernelGGL(reduce_rms_kernel<T>, dim3((unsigned)M), dim3(RMS_THREADS), 0, s, P, r4, o4, b4, H / 4,
-                           1.0f / (float)H, eps);
+        const dim3 grid((unsigned)M), block(RMS_THREADS);
+        if (stream)
+            hipLaunchKernelGGL((reduce_rms_kernel<T, true>), grid, block, 0, s, P, r4, o4, b4, H / 4, 1.0f / (float)H,
+                               eps);
+        else
+            hipLaunchKernelGGL((reduce_rms_kernel<T, false>), grid, block, 0, s, P, r4, o4, b4, H / 4, 1.0f / (float)H,
+                               eps);
     } else {
         const int64_t n4 = M * H / 4;
-        const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 1 << 16);
-        hipLaunchKernelGGL(reduce_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, P, r4, o4, b4, n4);
+        const dim3 grid((unsigned)std::min<int64_t>((n4 + 255) / 256, 1 << 16)), block(256);
+        if (stream)
+            hipLaunchKernelGGL((reduce_kernel<T, true>), grid, block, 0, s, P, r4, o4, b4, n4);
+        else
+            hipLaunchKernelGGL((reduce_kernel<T, false>), grid, block, 0, s, P, r4, o4, b4, n4);
     }
     return hipGetLastError();
 }

@@ -428,6 +428,29 @@ def test_reduce_rms_copy(H, inplace):
     assert rel_fro(to_f64(ob), wrms) <= TOL["bf16"]
 
 
+# partials larger than half the last-level cache (the 80-layer stack's
+# prefill reduces) are read with streaming loads: the same sums, exactly, in
+# place on the residual stream as the layer driver calls it, with and without
+# the row-RMS copy (ragged rows and a ragged last pass of the RMS kernel)
+@pytest.mark.parametrize("rms", [False, True])
+def test_reduce_streamed_partials(rms):
+    M, H, T = 1100, 4100, 8
+    assert T * M * H * 4 > 128 << 20
+    g = torch.Generator().manual_seed(11)
+    P = [torch.randint(-1000, 1000, (M, H), generator=g).float().cuda() for _ in range(T)]
+    R = torch.randint(-1000, 1000, (M, H), generator=g).float().cuda()
+    parts = np.stack([to_f64(p) for p in P])
+    ob = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    if rms:
+        want, wrms = oracle.shard_reduce(parts, to_f64(R), rms_eps=tp.TP_RMS_EPS)
+        tp.tp_shard_reduce(P, T, R, R, ob, M, H, tp.TP_REDUCE_RMS_BF16)
+        assert rel_fro(to_f64(ob), wrms) <= TOL["bf16"]
+    else:
+        want = oracle.shard_reduce(parts, to_f64(R))
+        tp.tp_shard_reduce(P, T, R, R, None, M, H)
+    assert np.array_equal(to_f64(R), want)
+
+
 # -------------------------------------------------------- edge cases
 def test_empty_call_touches_nothing():
     X = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
