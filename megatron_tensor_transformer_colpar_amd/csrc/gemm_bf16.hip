@@ -6,9 +6,12 @@
 // Design for gfx950 (CDNA4), one workgroup per BM x BN output tile, NW waves
 // (8 for the large tiles: two per SIMD, so one wave's MFMAs keep issuing
 // while the other waits on the issue of its loads; 4 for the small tile):
-//  * v_mfma_f32_32x32x16_bf16: the waves form a 2 x NW/2 grid, each owning a
-//    (BM/2) x (2*BN/NW) block of 32x32 accumulator tiles; 32x32 tiles need
-//    half the LDS fragment traffic of 16x16 tiles per flop.
+//  * The waves form a 2 x NW/2 grid, each owning a (BM/2) x (2*BN/NW) block
+//    of accumulator tiles: v_mfma_f32_16x16x32_bf16 for the forward and the
+//    input gradients (it holds a higher clock under the power cap than
+//    32x32x16, although 32x32 tiles need half the LDS fragment reads per
+//    flop), v_mfma_f32_32x32x16_bf16 for the weight gradients, whose two
+//    K-major operands would need more registers with 16x16 fragments.
 //  * K advances in BK-wide slices (BK = 64: 128 B per row, or 32) through a
 //    ring of S LDS stages filled by direct global->LDS DMA (buffer_load ...
 //    lds, 16 B per lane): no staging registers, no ds_write, and S-1 slices
@@ -108,17 +111,18 @@ struct Cfg {
 // banks once.  A K-major operand's k-rows are range-checked like rows, so
 // K need not be a multiple of BK.
 // The order of one 16x16x32 k-step, row by row: TN MFMAs, then the row's
-// fragment reads (its A fragment, and B fragment i while i < TN), then (RF)
+// fragment reads (its A fragment, and B fragment i while i < TN: RA and RB
+// LDS reads each, two for a K-major operand's transpose reads), then (RF)
 // its share of the refill DMA.
-template <int I, int TM, int TN, int DPR, int LOADS, bool RF>
+template <int I, int TM, int TN, int DPR, int LOADS, bool RF, int RA = 1, int RB = 1>
 __device__ __forceinline__ void pin_rows16()
 {
     if constexpr (I < TM) {
         __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, I < TN ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, I < TN ? RA + RB : RA, 0);
         if constexpr (RF && I * DPR < LOADS)
             __builtin_amdgcn_sched_group_barrier(0x020, ((I + 1) * DPR < LOADS ? (I + 1) * DPR : LOADS) - I * DPR, 0);
-        pin_rows16<I + 1, TM, TN, DPR, LOADS, RF>();
+        pin_rows16<I + 1, TM, TN, DPR, LOADS, RF, RA, RB>();
     }
 }
 
@@ -128,9 +132,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     using C_ = Cfg<BM, BN, BK, S, NW, MF>;
     constexpr int TM = C_::TM, TN = C_::TN, STAGE = C_::STAGE, CH = C_::CH, RB = C_::RB, KQ = C_::KQ;
     constexpr bool AKM = LAY == 2, BKM = LAY >= 1;   // K-major operands
-    static_assert(!(AKM || BKM) || (BK == 64 && BM >= 128 && BN >= 128 && NW % 2 == 0 && MF == 32),
-                  "K-major tile shape");
-    static_assert(MF == 32 || !epi_act_grad(EPI), "the gradient epilogues run with 32x32 tiles");
+    static_assert(!(AKM || BKM) || (BK == 64 && BM >= 128 && BN >= 128 && NW % 2 == 0), "K-major tile shape");
     using AccT = typename std::conditional<MF == 32, f32x16, f32x4>::type;
     // Gated: each wave's WTN rows of the B tile are WTN/2 gate rows followed
     // by the matching WTN/2 up rows, so accumulator tiles j and j + TN/2 of a
@@ -277,23 +279,39 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     const int a_base = (wm * C_::WTM + frow) * CH;
     const int b_base = (BM + wn * C_::WTN + frow) * CH;
 
-    // K-major fragment of 32-row block rb (r = rb + lane%32), k-step q: the
-    // transpose read e4 gives k = 16q + 8*fhalf + 4*e4 + 0..3; the addressing
-    // lane (i = lane%16) names k-row +i/4, 8 bytes at r = rb + 16*((lane/16)%2) + 4*(i%4).
+    // K-major fragment of MF-row block rb, k-step q, as two transpose reads
+    // e4 = 0, 1 (in a 16-lane group, lane i receives element i%4 of the
+    // 8-byte pieces addressed by lanes 4j + i/4, j = 0..3: four k-rows of the
+    // row i):
+    //   32x32x16: lane 32*fhalf + 16*g + i takes row rb + 16g + i, k = 16q +
+    //     8*fhalf + 4*e4 + 0..3; lane i addresses k-row +i/4, 8 bytes at
+    //     r = rb + 16g + 4*(i%4);
+    //   16x16x32: lane 16*kg + i takes row rb + i, k = 32q + 8*kg + 4*e4 +
+    //     0..3; lane i addresses k-row +i/4, 8 bytes at r = rb + 4*(i%4).
+    // The four k-rows of a group differ in k-row & 3, so the swizzle puts
+    // their 32 bytes in four different 64-byte spans: conflict-free.
     const int trr = (lane >> 2) & 3;
-    const int tr_lane = 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
-    int a_tr[TM], b_tr[TN];
+    const int tr_lane = MF == 32 ? 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1)
+                                 : 16 * ((lane & 3) >> 1) + 8 * (lane & 1);
+    // Offsets of the 32-row blocks; with 16x16 tiles block i is half i%2 of
+    // 32-row block i/2, 32 bytes on (bit 1 of the chunk index, which the
+    // swizzle leaves alone), so the offsets of half the blocks stay in
+    // registers and the rest fold into the reads' immediate offsets.
+    constexpr int TRM = MF == 16 ? TM / 2 : TM, TRN = MF == 16 ? TN / 2 : TN;
+    int a_tr[TRM], b_tr[TRN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) a_tr[i] = 16 * (((wm * C_::WTM + 32 * i) / 8) ^ (4 * trr)) + tr_lane;
+    for (int i = 0; i < TRM; ++i) a_tr[i] = 16 * (((wm * C_::WTM + 32 * i) / 8) ^ (4 * trr)) + tr_lane;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b_tr[j] = 16 * (((wn * C_::WTN + 32 * j) / 8) ^ (4 * trr)) + tr_lane;
+    for (int j = 0; j < TRN; ++j) b_tr[j] = 16 * (((wn * C_::WTN + 32 * j) / 8) ^ (4 * trr)) + tr_lane;
+    auto a_tro = [&](int i) __attribute__((always_inline)) { return MF == 16 ? a_tr[i >> 1] + 32 * (i & 1) : a_tr[i]; };
+    auto b_tro = [&](int j) __attribute__((always_inline)) { return MF == 16 ? b_tr[j >> 1] + 32 * (j & 1) : b_tr[j]; };
     // The reads index the stage in 8-byte elements (every offset here is a
     // multiple of 8): formed as byte offsets, the second read of each pair
     // lost track of which LDS array it reads, and the compiler made it wait
     // for every global->LDS load in flight, the next slices' included.
     auto tr_frag = [&](const u32x4 *region, int rowbytes, int off, int q) __attribute__((always_inline)) {
         const lds_bf16x4v *b8 = reinterpret_cast<const lds_bf16x4v *>(LDS_PTR(region));
-        const int k0 = 16 * q + 8 * fhalf + trr;
+        const int k0 = MF == 32 ? 16 * q + 8 * fhalf + trr : 32 * q + 8 * (lane >> 4) + trr;
         const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(b8 + ((k0 * rowbytes + off) >> 3)));
         const bf16x4v hi =
             __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4v *)(b8 + (((k0 + 4) * rowbytes + off) >> 3)));
@@ -308,14 +326,14 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             if constexpr (AKM)
-                fa[p][i] = tr_frag(sa, BM * 2, a_tr[i], q);
+                fa[p][i] = tr_frag(sa, BM * 2, a_tro(i), q);
             else
                 fa[p][i] = __builtin_bit_cast(bf16x8, sa[a_base + i * MF * CH + slot]);
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             if constexpr (BKM)
-                fb[p][j] = tr_frag(sb, BN * 2, b_tr[j], q);
+                fb[p][j] = tr_frag(sb, BN * 2, b_tro(j), q);
             else
                 fb[p][j] = __builtin_bit_cast(bf16x8, sb[b_off + j * MF * CH + slot]);
         }
@@ -412,7 +430,7 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     // fragments stay double-buffered.  Each row of MFMAs is followed by its
     // reads and, in the step after the barrier, by its share of the refill
     // DMA; sched_group_barriers pin that order.
-    static_assert(MF == 32 || (KQ == 2 && TN <= TM && !AKM && !BKM), "16x16x32 main loop shape");
+    static_assert(MF == 32 || (KQ == 2 && TN <= TM), "16x16x32 main loop shape");
     constexpr int DPR = (C_::LOADS + TM - 1) / TM;   // refill DMA instructions per row
     // step16 reads k-step rq of the A and B slices at ra, rb and (refill)
     // issues A slice kta into fa_st and B slice ktb into fb_st
@@ -426,12 +444,20 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[pm][j], fa[0][i], acc[i][j], 0, 0, 0);
-                fa[0][i] = __builtin_bit_cast(bf16x8, ra[a_base + i * MF * CH + slot]);
-                if (i < TN) fb[pr][i] = __builtin_bit_cast(bf16x8, rb[b_off + i * MF * CH + slot]);
+                if constexpr (AKM)
+                    fa[0][i] = tr_frag(ra, BM * 2, a_tro(i), rq);
+                else
+                    fa[0][i] = __builtin_bit_cast(bf16x8, ra[a_base + i * MF * CH + slot]);
+                if (i < TN) {
+                    if constexpr (BKM)
+                        fb[pr][i] = tr_frag(rb, BN * 2, b_tro(i), rq);
+                    else
+                        fb[pr][i] = __builtin_bit_cast(bf16x8, rb[b_off + i * MF * CH + slot]);
+                }
                 if constexpr (RF)
                     issue_part(fa_st, fb_st, kta, ktb, i * DPR, min((i + 1) * DPR, C_::LOADS));
             }
-            pin_rows16<0, TM, TN, DPR, C_::LOADS, RF>();
+            pin_rows16<0, TM, TN, DPR, C_::LOADS, RF, AKM ? 2 : 1, BKM ? 2 : 1>();
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -472,8 +498,16 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
         const int slot0 = fq ^ fsw;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            fa[0][i] = __builtin_bit_cast(bf16x8, ring_a[0][a_base + i * MF * CH + slot0]);
-            if (i < TN) fb[0][i] = __builtin_bit_cast(bf16x8, ring_b[0][b_off + i * MF * CH + slot0]);
+            if constexpr (AKM)
+                fa[0][i] = tr_frag(ring_a[0], BM * 2, a_tro(i), 0);
+            else
+                fa[0][i] = __builtin_bit_cast(bf16x8, ring_a[0][a_base + i * MF * CH + slot0]);
+            if (i < TN) {
+                if constexpr (BKM)
+                    fb[0][i] = tr_frag(ring_b[0], BN * 2, b_tro(i), 0);
+                else
+                    fb[0][i] = __builtin_bit_cast(bf16x8, ring_b[0][b_off + i * MF * CH + slot0]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     } else {
@@ -749,10 +783,13 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
     // bit-identical.
     g.bands = EPI == EPI_STORE_F32 && LAY == 0 && BM == 256 && BN == 256 && g.tiles_n % 8 == 0 && g.tiles_n >= 32;
     const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(NW * 64);
-    // K-contiguous operands (the forward) run on 16x16x32 MFMAs, the K-major
-    // layouts of the backward on 32x32x16 (their transpose reads are laid out
-    // for 32-row fragments)
-    constexpr int MF = LAY == 0 ? 16 : 32;
+    // 16x16x32 MFMAs draw less power per flop than 32x32x16 and hold a
+    // higher clock under the power cap.  The weight gradients (both operands
+    // K-major) stay on 32x32x16: with 16x16 fragments their transpose reads
+    // need more than 256 registers and spill, and the backward at the
+    // prefill shape took 2398 against 2158 us; the input gradients (one
+    // K-major operand) took it from 2158 to 2111 us, bitwise equal.
+    constexpr int MF = LAY == 2 ? 32 : 16;
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY, NTS, MF, DB>), grid, block, 0, s, g);
     return hipGetLastError();
 }
