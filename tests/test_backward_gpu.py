@@ -230,6 +230,39 @@ def test_backward_full_size_sampled():
     assert er <= TOL["bf16"]
 
 
+def test_backward_prefill_rank_shape_sampled():
+    # rank 0 of the pages' prefill shape (H=8192, F/T=4096, M=8192), as the
+    # bench times it: every launch on 256x256 tiles, dU and dX on 16x16x32
+    # transpose-read fragments, dW1 and dW2 on 32x32x16; sampled gradient
+    # columns (first and last included) and sampled dX rows against the oracle
+    w = inputs.WORKLOADS["prefill"]
+    M, H, Fs = w.M, w.H, w.F // w.T
+    X, W1, b1, W2 = inputs.mlp_inputs(w, shard_only=0)
+    dZ = inputs.normal((M, H), 1.0, "bf16", seed=0, workload=w.wid, tensor=DZ_ID)
+    dX_, dW1t_, db1_, dW2t_ = X.torch(), W1.transposed().torch(), b1.torch(), W2.transposed().torch()
+    Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+    U = torch.empty_like(Y)
+    dU = torch.empty_like(Y)
+    dX = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    dW1t = torch.empty(Fs, H, dtype=torch.float32, device="cuda")
+    db1 = torch.empty(Fs, dtype=torch.float32, device="cuda")
+    dW2t = torch.empty(H, Fs, dtype=torch.float32, device="cuda")
+    tp.tp_colpar_act_train(dX_, dW1t_, db1_, Y, U, M, H, Fs, 1, 0)
+    tp.tp_mlp_shard_bwd(dX_, dW1t_, dW2t_, U, Y, dZ.torch(), dU, dX, dW1t, db1, dW2t, M, H, Fs, 1, 0)
+    torch.cuda.synchronize()
+    cols = inputs.row_sample(Fs, 8, seed=5)
+    oc = oracle.mlp_shard_bwd(X.f64, W1.f64[:, cols], b1.f64[cols], W2.f64[cols], dZ.f64, 1, 0)
+    e = (rel_fro(to_f64(dU)[:, cols], oc["dU_i"]), rel_fro(to_f64(dW1t)[cols].T, oc["dW1_i"]),
+         rel_fro(to_f64(db1)[cols], oc["db1_i"]), rel_fro(to_f64(dW2t)[:, cols].T, oc["dW2_i"]))
+    print("  columns: dU %.2e dW1 %.2e db1 %.2e dW2 %.2e" % e)
+    assert max(e) <= TOL["bf16"]
+    rows = inputs.row_sample(M, 16, seed=6)
+    orow = oracle.mlp_shard_bwd(X.f64[rows], W1.f64, b1.f64, W2.f64, dZ.f64[rows], 1, 0)
+    er = rel_fro(to_f64(dX)[rows], orow["dX_i"])
+    print("  rows: dX %.2e" % er)
+    assert er <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("T,M", [(4, 256), (2, 130)])
 def test_group_entry_points(T, M):
     # the whole group's training forward and backward, one launch per
