@@ -11,7 +11,7 @@
 // Partials larger than half the 256 MB last-level cache are read with
 // non-temporal loads: they cannot stay cached anyway, and at the 80-layer
 // stack's prefill shape (eight 128 MiB partials and the residual, in place)
-// the plain reduce took 214 instead of 258 us with them (6.3 against 5.2
+// the plain reduce took 221 instead of 258 us with them (6.1 against 5.2
 // TB/s); partials the cache does hold (the 2048-token block's four) are
 // read faster through it.
 #include "device_common.h"
