@@ -24,7 +24,8 @@
 //   attention recurrence (Dao et al., arXiv:2205.14135).
 // * attn_decode_kernel (a few rows: decode), memory-bound: the keys of a
 //   sequence are split into chunks spread over many workgroups; each streams
-//   its chunk of K and then of V once, 16 lanes per 256-byte row, and writes
+//   its chunk of K and then of V once (the V rows of its first 64 keys
+//   requested with their K rows), 16 lanes per 256-byte row, and writes
 //   an unnormalised partial (max, sum, weighted values).  Each workgroup then
 //   counts its arrival for its (sequence, key/value head); the last to
 //   arrive merges the chunks of those query rows in chunk order and resets
@@ -383,13 +384,26 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, 
         make_rsrc(vb_, nk > 0 ? (uint32_t)(((int64_t)(nk - 1) * a.ldv + kD) * 2) : 0u);
     const uint32_t lane_b = 16u * cc;
 
-    // scores: wave w takes keys 16i + 4w + kk, four rows in flight per lane
+    // scores: wave w takes keys 16i + 4w + kk, four rows in flight per lane.
+    // The value rows of the first 64 keys do not depend on the scores: they
+    // are requested right behind their key rows, so a 64-key chunk (one
+    // sequence) streams its values under the scores and the softmax
+    // (12.53 -> 11.89 us at one sequence, bitwise equal; 8 and 32 sequences
+    // unchanged).
+    u32x4 vfirst[4];
     for (int base = 0; base < nk; base += 64) {
         u32x4 kr[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int t = base + 16 * u + 4 * wave + kk;
             kr[u] = buf_load16(rk, (uint32_t)(t * a.ldk * 2) + lane_b, 0);
+        }
+        if (base == 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = 16 * u + 4 * wave + kk;
+                vfirst[u] = buf_load16(rv, (uint32_t)(t * a.ldv * 2) + lane_b, 0);
+            }
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -443,7 +457,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, 
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int t = base + 16 * u + 4 * wave + kk;
-            vr[u] = buf_load16(rv, (uint32_t)(t * a.ldv * 2) + lane_b, 0);
+            vr[u] = base == 0 ? vfirst[u] : buf_load16(rv, (uint32_t)(t * a.ldv * 2) + lane_b, 0);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
