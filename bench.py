@@ -314,7 +314,10 @@ def gpt_block_shard(args, torch, tp, inputs):
 def variants(args, torch, tp):
     """The exact-GeLU and gated Gate/Up first layers of rank 0: prefill at
     H=8192, F/T=4096, M=8192 (TFLOP/s; gated counts both projections) and the
-    gated decode step at M=8 over rotating weight sets (weight GB/s)."""
+    gated decode step at M=8 over rotating weight sets (weight GB/s).  Each
+    figure is the median of 20 timed trials (one pass's mean is fragile
+    against a single stall of the GPU at these call lengths); the decode
+    step's pass mean is kept beside it."""
     g = torch.Generator(device="cuda").manual_seed(9)
     stream = torch.cuda.current_stream().cuda_stream
     H, Fs = 8192, 4096
@@ -322,37 +325,46 @@ def variants(args, torch, tp):
     def bf(*shape, std=1.0):
         return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
 
-    def timed(f, n):
-        warm(torch, f)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for k in range(n):
-            f(k)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+    def median_ms(f, per):
+        ctr = [0]
+
+        def call():
+            f(ctr[0])
+            ctr[0] += 1
+        warm(torch, lambda k: call())
+        return trials(torch, call, n_trials=20, per=per)["median_ms"]
 
     out = {}
     M = 8192
     X, Wg, Wu, bg, bu = bf(M, H), bf(Fs, H, std=0.02), bf(Fs, H, std=0.02), bf(Fs, std=0.01), bf(Fs, std=0.01)
     Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
-    n = max(3, args.steps // 5)
     fl = 2.0 * M * H * Fs
-    ms = timed(lambda k: tp.tp_colpar_act(X, Wg, bg, Y, M, H, Fs, 1, 0, tp.TP_GELU_ERF, tp.TP_BF16, stream), n)
+    ms = median_ms(lambda k: tp.tp_colpar_act(X, Wg, bg, Y, M, H, Fs, 1, 0, tp.TP_GELU_ERF, tp.TP_BF16, stream), 3)
     out["prefill_exact_gelu_tflops"] = round(fl / (ms * 1e-3) / 1e12, 1)
-    ms = timed(lambda k: tp.tp_colpar_gated(X, Wg, Wu, bg, bu, Y, M, H, Fs, 1, 0, tp.TP_GELU_TANH, tp.TP_BF16,
-                                            stream), n)
+    ms = median_ms(lambda k: tp.tp_colpar_gated(X, Wg, Wu, bg, bu, Y, M, H, Fs, 1, 0, tp.TP_GELU_TANH, tp.TP_BF16,
+                                                stream), 3)
     out["prefill_gated_tflops"] = round(2 * fl / (ms * 1e-3) / 1e12, 1)
     del X, Y
     M, R = 8, args.decode_sets
     sets = [(bf(Fs, H, std=0.02), bf(Fs, H, std=0.02)) for _ in range(R)]
     X = bf(M, H)
     Y = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
-    ms = timed(lambda k: tp.tp_colpar_gated(X, sets[k % R][0], sets[k % R][1], bg, bu, Y, M, H, Fs, 1, 0,
-                                            tp.TP_GELU_TANH, tp.TP_BF16, stream), max(2 * R, args.steps))
+
+    def gated_decode(k):
+        tp.tp_colpar_gated(X, sets[k % R][0], sets[k % R][1], bg, bu, Y, M, H, Fs, 1, 0, tp.TP_GELU_TANH,
+                           tp.TP_BF16, stream)
+    ms = median_ms(gated_decode, R)
+    n = max(2 * R, args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for k in range(n):
+        gated_decode(k)
+    e1.record()
+    torch.cuda.synchronize()
     by = 2.0 * (2 * Fs * H + 2 * Fs) + M * H * 2 + M * Fs * 2
     out["decode_gated_m8_us"] = round(ms * 1e3, 2)
+    out["decode_gated_m8_pass_mean_us"] = round(e0.elapsed_time(e1) / n * 1e3, 2)
     out["decode_gated_m8_gbs"] = round(by / (ms * 1e-3) / 1e9, 1)
     out["decode_gated_m8_frac"] = round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
     out["workload"] = "rank 0 first layer, H=8192 F/T=4096: prefill M=8192, decode M=8"
