@@ -7,11 +7,10 @@
 // (8 for the large tiles: two per SIMD, so one wave's MFMAs keep issuing
 // while the other waits on the issue of its loads; 4 for the small tile):
 //  * The waves form a 2 x NW/2 grid, each owning a (BM/2) x (2*BN/NW) block
-//    of accumulator tiles: v_mfma_f32_16x16x32_bf16 for the forward and the
-//    input gradients (it holds a higher clock under the power cap than
-//    32x32x16, although 32x32 tiles need half the LDS fragment reads per
-//    flop), v_mfma_f32_32x32x16_bf16 for the weight gradients, whose two
-//    K-major operands would need more registers with 16x16 fragments.
+//    of accumulator tiles on v_mfma_f32_16x16x32_bf16 (it holds a higher
+//    clock under the power cap than 32x32x16, although 32x32 tiles need half
+//    the LDS fragment reads per flop); accumulating weight gradients use
+//    v_mfma_f32_32x32x16_bf16, whose fragments need fewer registers.
 //  * K advances in BK-wide slices (BK = 64: 128 B per row, or 32) through a
 //    ring of S LDS stages filled by direct global->LDS DMA (buffer_load ...
 //    lds, 16 B per lane): no staging registers, no ds_write, and S-1 slices
@@ -114,6 +113,34 @@ struct Cfg {
 // fragment reads (its A fragment, and B fragment i while i < TN: RA and RB
 // LDS reads each, two for a K-major operand's transpose reads), then (RF)
 // its share of the refill DMA.
+// With single-buffered B fragments (both operands K-major): rows 0 .. TM-2
+// are TN MFMAs and the row's A fragment read; the last row reads B fragment
+// j of the next k-step right behind MFMA j, then its A fragment.
+template <int J, int TN, int RB>
+__device__ __forceinline__ void pin_last_row_sb()
+{
+    if constexpr (J < TN) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);
+        pin_last_row_sb<J + 1, TN, RB>();
+    }
+}
+template <int I, int TM, int TN, int DPR, int LOADS, bool RF, int RA, int RB>
+__device__ __forceinline__ void pin_rows16_sb()
+{
+    if constexpr (I < TM) {
+        if constexpr (I + 1 < TM) {
+            __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+        } else {
+            pin_last_row_sb<0, TN, RB>();
+            __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);
+        }
+        if constexpr (RF && I * DPR < LOADS)
+            __builtin_amdgcn_sched_group_barrier(0x020, ((I + 1) * DPR < LOADS ? (I + 1) * DPR : LOADS) - I * DPR, 0);
+        pin_rows16_sb<I + 1, TM, TN, DPR, LOADS, RF, RA, RB>();
+    }
+}
 template <int I, int TM, int TN, int DPR, int LOADS, bool RF, int RA = 1, int RB = 1>
 __device__ __forceinline__ void pin_rows16()
 {
@@ -427,7 +454,13 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     // beside its 128 accumulator registers (two waves per SIMD), so the A
     // fragments are single-buffered: A fragment i of the next k-step is read
     // right after the MFMAs of row i (its last use) are issued; the B
-    // fragments stay double-buffered.  Each row of MFMAs is followed by its
+    // fragments stay double-buffered, except with both operands K-major
+    // (the weight gradients), whose transpose reads need the registers: there
+    // B fragment j of the next k-step is read right after the last row's
+    // MFMA j (with double-buffered B they spilled 16-20 registers, whose
+    // reloads in the main loop waited on the DMA's counter; the backward at
+    // the prefill shape took 2096 against 2129 us on 32x32x16 and 2398 us
+    // with the spills, bitwise equal).  Each row of MFMAs is followed by its
     // reads and, in the step after the barrier, by its share of the refill
     // DMA; sched_group_barriers pin that order.
     static_assert(MF == 32 || (KQ == 2 && TN <= TM), "16x16x32 main loop shape");
@@ -437,7 +470,27 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     auto step16 = [&](auto refill_tag, const u32x4 *ra, const u32x4 *rb, int rq, int pm, int pr, u32x4 *fa_st,
                       u32x4 *fb_st, int kta, int ktb) __attribute__((always_inline)) {
         constexpr bool RF = decltype(refill_tag)::value;
-        if constexpr (MF == 16) {
+        if constexpr (MF == 16 && AKM && BKM) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                if (i + 1 < TM) {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[0][j], fa[0][i], acc[i][j], 0, 0, 0);
+                        fb[0][j] = tr_frag(rb, BN * 2, b_tro(j), rq);
+                    }
+                }
+                fa[0][i] = tr_frag(ra, BM * 2, a_tro(i), rq);
+                if constexpr (RF)
+                    issue_part(fa_st, fb_st, kta, ktb, i * DPR, min((i + 1) * DPR, C_::LOADS));
+            }
+            pin_rows16_sb<0, TM, TN, DPR, C_::LOADS, RF, 2, 2>();
+            __builtin_amdgcn_sched_barrier(0);
+        } else if constexpr (MF == 16) {
             const int slot = (C_::CPQ * rq + fq) ^ fsw;
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
@@ -784,12 +837,13 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
     g.bands = EPI == EPI_STORE_F32 && LAY == 0 && BM == 256 && BN == 256 && g.tiles_n % 8 == 0 && g.tiles_n >= 32;
     const dim3 grid((unsigned)(g.batch * g.tiles_m * g.tiles_n)), block(NW * 64);
     // 16x16x32 MFMAs draw less power per flop than 32x32x16 and hold a
-    // higher clock under the power cap.  The weight gradients (both operands
-    // K-major) stay on 32x32x16: with 16x16 fragments their transpose reads
-    // need more than 256 registers and spill, and the backward at the
-    // prefill shape took 2398 against 2158 us; the input gradients (one
-    // K-major operand) took it from 2158 to 2111 us, bitwise equal.
-    constexpr int MF = LAY == 2 ? 32 : 16;
+    // higher clock under the power cap: the input gradients (one K-major
+    // operand) took the backward at the prefill shape from 2158 to 2111 us
+    // with them, bitwise equal, and the weight gradients (single-buffered B
+    // fragments, see the main loop) from 2129 to 2096 us.  Accumulating
+    // weight gradients stay on 32x32x16: their epilogue's extra registers
+    // still leave reloads in the 16x16 main loop.
+    constexpr int MF = LAY == 2 && EPI == EPI_ACC_F32 ? 32 : 16;
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY, NTS, MF, DB>), grid, block, 0, s, g);
     return hipGetLastError();
 }
