@@ -263,6 +263,36 @@ def test_backward_prefill_rank_shape_sampled():
     assert er <= TOL["bf16"]
 
 
+def test_weight_gradients_on_256x128_tiles():
+    # H=4096, F/T=2048: the weight gradients (2048 x 4096 and 4096 x 2048)
+    # are 128 tiles of 256x256 but 256 of 256x128, so they take the 256x128
+    # tile (two B fragments per wave, single-buffered); 520 tokens make their
+    # K ragged (8 slices of 64 and 8 left over); sampled gradient columns,
+    # exact on their own, against the oracle
+    M, H, F, T = 520, 4096, 4096, 2
+    p = Problem(77, M, H, F, T, ERF)
+    Fs = p.Fs
+    i = 1
+    Y, U = p.forward_train(i)
+    dU = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    # the full gradients: rank i writes its block (rows C_i of dW1^T, entries
+    # C_i of db1, columns C_i of dW2^T)
+    dW1t = torch.zeros(F, H, dtype=torch.float32, device="cuda")
+    db1 = torch.zeros(F, dtype=torch.float32, device="cuda")
+    dW2t = torch.zeros(H, F, dtype=torch.float32, device="cuda")
+    tp.tp_mlp_shard_bwd(p.dX_, p.dW1t, p.dW2t, U, Y, p.ddZ, dU, dX, dW1t, db1, dW2t, M, H, F, T, i,
+                        act_code(ERF))
+    torch.cuda.synchronize()
+    cols = inputs.row_sample(Fs, 12, seed=7)
+    gcols = i * Fs + cols
+    oc = oracle.mlp_shard_bwd(p.X.f64, p.W1.f64[:, gcols], p.b1.f64[gcols], p.W2.f64[gcols], p.dZ.f64, 1, 0, ERF)
+    e = (rel_fro(to_f64(dU)[:, cols], oc["dU_i"]), rel_fro(to_f64(dW1t)[gcols].T, oc["dW1_i"]),
+         rel_fro(to_f64(db1)[gcols], oc["db1_i"]), rel_fro(to_f64(dW2t)[:, gcols].T, oc["dW2_i"]))
+    print("  columns: dU %.2e dW1 %.2e db1 %.2e dW2 %.2e" % e)
+    assert max(e) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("T,M", [(4, 256), (2, 130)])
 def test_group_entry_points(T, M):
     # the whole group's training forward and backward, one launch per
