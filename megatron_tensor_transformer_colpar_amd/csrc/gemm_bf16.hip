@@ -9,8 +9,8 @@
 //  * The waves form a 2 x NW/2 grid, each owning a (BM/2) x (2*BN/NW) block
 //    of accumulator tiles on v_mfma_f32_16x16x32_bf16 (it holds a higher
 //    clock under the power cap than 32x32x16, although 32x32 tiles need half
-//    the LDS fragment reads per flop); accumulating weight gradients use
-//    v_mfma_f32_32x32x16_bf16, whose fragments need fewer registers.
+//    the LDS fragment reads per flop).  The kernel still takes MF = 32
+//    (v_mfma_f32_32x32x16_bf16), which no launch uses.
 //  * K advances in BK-wide slices (BK = 64: 128 B per row, or 32) through a
 //    ring of S LDS stages filled by direct global->LDS DMA (buffer_load ...
 //    lds, 16 B per lane): no staging registers, no ds_write, and S-1 slices
@@ -82,6 +82,17 @@ __device__ __forceinline__ int op_swz(int row)
     return swz<CH>(row);
 }
 
+// K-major operand tiles: chunk c of k-row kr sits at slot c ^ kmaj_swz(kr).
+// A fragment's transpose reads take four consecutive k-rows per 16-lane
+// group, and gfx950 serves the two groups eight k-rows apart together:
+// 4(kr & 3) puts one group's four k-rows in four 64-byte spans, 2(kr >> 3 & 1)
+// moves the other group's to the other 32 bytes of each, so the 32 lanes
+// cover all banks once.  An LDS probe of these reads measured 1.59 ns per
+// ds_read_b64_tr_b16 per CU, against 2.19 ns with 4(kr & 3) alone and 1.57
+// ns for 64 lanes reading 512 contiguous bytes.  Bits 0, 1 and 3 only: the
+// second read of a fragment (four k-rows on) sees the same swizzle.
+__device__ __forceinline__ int kmaj_swz(int kr) { return (4 * (kr & 3)) ^ (2 * ((kr >> 3) & 1)); }
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt_hi[15:14],
 // expcnt[6:4], lgkmcnt[11:8]).
 __host__ __device__ constexpr int wait_vm_lgkm0(int vm)
@@ -116,12 +127,11 @@ struct Cfg {
 // k * ld + r, as for an activation read along its token axis (the weight
 // gradients) or a K-contiguous weight read along its output axis (the input
 // gradients).  A K-major tile is BK rows (k) of BM (or BN) values; chunk c
-// of k-row kr sits at slot c ^ 4(kr & 3), and an MFMA fragment (8 k values
-// of one r) is two LDS transpose reads (ds_read_b64_tr_b16: in a 16-lane
-// group, lane i gets element i%4 of the 8-byte rows addressed by lanes
-// 4j + i/4); the 4 k-rows x 64 bytes a half-wave reads then cover all 64
-// banks once.  A K-major operand's k-rows are range-checked like rows, so
-// K need not be a multiple of BK.
+// of k-row kr sits at slot c ^ kmaj_swz(kr), and an MFMA fragment (8 k
+// values of one r) is two LDS transpose reads (ds_read_b64_tr_b16: in a
+// 16-lane group, lane i gets element i%4 of the 8-byte rows addressed by
+// lanes 4j + i/4).  A K-major operand's k-rows are range-checked like rows,
+// so K need not be a multiple of BK.
 // The order of one 16x16x32 k-step, row by row: TN MFMAs, then the row's
 // fragment reads (its A fragment, and B fragment i while i < TN: RA and RB
 // LDS reads each, two for a K-major operand's transpose reads), then (RF)
@@ -243,11 +253,14 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     // K-major tiles: a 1 KiB block is KRA (KRB) k-rows of BM/8 (BN/8)
     // chunks; instruction j of wave w fills block NW*j + w, lane L lands in
     // k-row L/(BM/8) of it, physical chunk L%(BM/8), and fetches the logical
-    // chunk the swizzle puts there (k-row & 3 does not depend on j).
+    // chunk the swizzle puts there (j moves the k-row by a multiple of 16,
+    // so kmaj_swz does not depend on j).
     constexpr int ACH = BM / 8, BCH = BN / 8, KRA = 64 / ACH, KRB = 64 / BCH;
+    static_assert(!AKM || (NW * KRA) % 16 == 0, "K-major A: the DMA step keeps k-row bits 0..3");
+    static_assert(!BKM || (NW * KRB) % 16 == 0, "K-major B: the DMA step keeps k-row bits 0..3");
     const int a_krow = wave * KRA + lane / ACH, b_krow = wave * KRB + lane / BCH;
-    const uint32_t ak_voff = (uint32_t)((a_krow * g.lda + 8 * ((lane % ACH) ^ (4 * (a_krow & 3)))) * 2);
-    const uint32_t bk_voff = (uint32_t)((b_krow * g.ldb + 8 * ((lane % BCH) ^ (4 * (b_krow & 3)))) * 2);
+    const uint32_t ak_voff = (uint32_t)((a_krow * g.lda + 8 * ((lane % ACH) ^ kmaj_swz(a_krow))) * 2);
+    const uint32_t bk_voff = (uint32_t)((b_krow * g.ldb + 8 * ((lane % BCH) ^ kmaj_swz(b_krow))) * 2);
     const uint32_t ak_jstep = (uint32_t)(NW * KRA * g.lda * 2), bk_jstep = (uint32_t)(NW * KRB * g.ldb * 2);
     const int KT = (AKM || BKM) ? (g.K + BK - 1) / BK : g.K / BK;
     // Gated B rows: instruction j of this wave fills tile rows r0 .. r0+RB-1,
@@ -327,23 +340,24 @@ __global__ void __launch_bounds__(NW * 64) gemm_bf16_kernel(GemmDev g)
     //     r = rb + 16g + 4*(i%4);
     //   16x16x32: lane 16*kg + i takes row rb + i, k = 32q + 8*kg + 4*e4 +
     //     0..3; lane i addresses k-row +i/4, 8 bytes at r = rb + 4*(i%4).
-    // The four k-rows of a group differ in k-row & 3, so the swizzle puts
-    // their 32 bytes in four different 64-byte spans: conflict-free.
+    // The lane's k-rows have bits 0..1 = trr and bit 3 = its 16-lane group's
+    // parity (16x16x32) or its k half (32x32x16); kmaj_swz of those places
+    // the 32 lanes of two groups on all banks once.
     const int trr = (lane >> 2) & 3;
-    const int tr_lane = MF == 32 ? 16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1)
-                                 : 16 * ((lane & 3) >> 1) + 8 * (lane & 1);
-    // Offsets of the 32-row blocks; with 16x16 tiles block i is half i%2 of
-    // 32-row block i/2, 32 bytes on (bit 1 of the chunk index, which the
-    // swizzle leaves alone), so the offsets of half the blocks stay in
-    // registers and the rest fold into the reads' immediate offsets.
+    const int tsw = kmaj_swz(trr + 8 * (MF == 32 ? (lane >> 5) & 1 : (lane >> 4) & 1));
+    const int tr_chunk = MF == 32 ? 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1) : (lane & 3) >> 1;
+    // Byte offsets of the 32-row blocks (their first chunk is a multiple of
+    // 4); with 16x16 tiles block i is half i%2 of 32-row block i/2, two
+    // chunks on, i.e. the same offset with bit 5 flipped, so the offsets of
+    // half the blocks stay in registers.
     constexpr int TRM = MF == 16 ? TM / 2 : TM, TRN = MF == 16 ? TN / 2 : TN;
     int a_tr[TRM], b_tr[TRN];
 #pragma unroll
-    for (int i = 0; i < TRM; ++i) a_tr[i] = 16 * (((wm * C_::WTM + 32 * i) / 8) ^ (4 * trr)) + tr_lane;
+    for (int i = 0; i < TRM; ++i) a_tr[i] = 16 * (((wm * C_::WTM + 32 * i) / 8 + tr_chunk) ^ tsw) + 8 * (lane & 1);
 #pragma unroll
-    for (int j = 0; j < TRN; ++j) b_tr[j] = 16 * (((wn * C_::WTN + 32 * j) / 8) ^ (4 * trr)) + tr_lane;
-    auto a_tro = [&](int i) __attribute__((always_inline)) { return MF == 16 ? a_tr[i >> 1] + 32 * (i & 1) : a_tr[i]; };
-    auto b_tro = [&](int j) __attribute__((always_inline)) { return MF == 16 ? b_tr[j >> 1] + 32 * (j & 1) : b_tr[j]; };
+    for (int j = 0; j < TRN; ++j) b_tr[j] = 16 * (((wn * C_::WTN + 32 * j) / 8 + tr_chunk) ^ tsw) + 8 * (lane & 1);
+    auto a_tro = [&](int i) __attribute__((always_inline)) { return MF == 16 ? a_tr[i >> 1] ^ (32 * (i & 1)) : a_tr[i]; };
+    auto b_tro = [&](int j) __attribute__((always_inline)) { return MF == 16 ? b_tr[j >> 1] ^ (32 * (j & 1)) : b_tr[j]; };
     // The reads index the stage in 8-byte elements (every offset here is a
     // multiple of 8): formed as byte offsets, the second read of each pair
     // lost track of which LDS array it reads, and the compiler made it wait
@@ -853,9 +867,11 @@ hipError_t launch_one(const GemmArgs &a, hipStream_t s)
     // operand) took the backward at the prefill shape from 2158 to 2111 us
     // with them, bitwise equal, and the weight gradients (single-buffered B
     // fragments, see the main loop) from 2129 to 2096 us.  Accumulating
-    // weight gradients stay on 32x32x16: their epilogue's extra registers
-    // still leave reloads in the 16x16 main loop.
-    constexpr int MF = LAY == 2 && EPI == EPI_ACC_F32 ? 32 : 16;
+    // weight gradients followed once the conflict-free K-major layout freed
+    // the registers their epilogue needs: 2180.2 -> 2149.4 us for the
+    // forward and the accumulating backward at the prefill shape, bitwise
+    // equal.
+    constexpr int MF = 16;
     hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, S, NW, IL, EPI, LAY, NTS, MF, DB>), grid, block, 0, s, g);
     return hipGetLastError();
 }
