@@ -381,7 +381,8 @@ def attention(args, torch, tp):
     token each: the Q/K/V projection writing the new key and value rows into
     the caches, and split-key attention over the caches (HBM GB/s of weights
     or cache bytes; weight sets and caches rotate over more than 1 GiB, so
-    every call streams from HBM)."""
+    every call streams from HBM; medians of 20 trials, since a single mean
+    of these short calls moved by half between runs)."""
     g = torch.Generator(device="cuda").manual_seed(11)
     stream = torch.cuda.current_stream().cuda_stream
     H, As, D, nh = 8192, 1024, 128, 8
@@ -399,6 +400,15 @@ def attention(args, torch, tp):
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
+
+    def median_ms(f, per):
+        ctr = [0]
+
+        def call():
+            f(ctr[0])
+            ctr[0] += 1
+        warm(torch, lambda k: call())
+        return trials(torch, call, n_trials=20, per=per)["median_ms"]
 
     def rate(flops, ms):
         t = flops / (ms * 1e-3) / 1e12
@@ -458,10 +468,9 @@ def attention(args, torch, tp):
             kc, vc = caches[k % C]
             tp.tp_attn_core(Q, kc, vc, ctx, None, Bs, 1, L, nh, nh, D, As, As, As, 1, ws, nws, stream)
 
-        nd = max(2 * max(R, C), args.steps)
         wbytes = 3.0 * (As * H * 2 + As * 2) + Bs * H * 2 + 3 * Bs * As * 2
-        e = {"qkv_projection": bw(wbytes, timed(qkv, nd)),
-             "attention_core": bw(cache_bytes + 2.0 * Bs * As * 2, timed(core, nd)),
+        e = {"qkv_projection": bw(wbytes, median_ms(qkv, max(R, C))),
+             "attention_core": bw(cache_bytes + 2.0 * Bs * As * 2, median_ms(core, C)),
              "cache_bytes": cache_bytes}
         dec["M=%d" % Bs] = e
         log("[bench] attention decode M=%d: %s" % (Bs, e))
