@@ -386,10 +386,11 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, 
 
     // scores: wave w takes keys 16i + 4w + kk, four rows in flight per lane.
     // The value rows of the first 64 keys do not depend on the scores: they
-    // are requested right behind their key rows, so a 64-key chunk (one
-    // sequence) streams its values under the scores and the softmax
-    // (12.53 -> 11.89 us at one sequence, bitwise equal; 8 and 32 sequences
-    // unchanged).
+    // are requested right behind their key rows and stream under the scores
+    // and the softmax (one sequence in 64-key chunks: 12.53 -> 11.89 us,
+    // bitwise equal; 8 and 32 sequences unchanged).  Requesting the next 64
+    // keys' values as well was slower (11.95 against 11.46 us in 128-key
+    // chunks).
     u32x4 vfirst[4];
     for (int base = 0; base < nk; base += 64) {
         u32x4 kr[4];
