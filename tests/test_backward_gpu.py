@@ -293,6 +293,39 @@ def test_weight_gradients_on_256x128_tiles():
     assert max(e) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("F", [8192, 4096])
+def test_weight_gradients_accumulate_on_large_tiles(F):
+    # H=4096, T=2: F/T = 4096 makes the weight gradients 256 tiles of
+    # 256x256, F/T = 2048 makes them 256 of 256x128; 520 tokens make their K
+    # ragged.  Accumulating into random gradients: the increments of rank i's
+    # sampled columns against the oracle, everything outside rank i's blocks
+    # untouched
+    M, H, T = 520, 4096, 2
+    p = Problem(78, M, H, F, T)
+    Fs = p.Fs
+    i = 1
+    Y, U = p.forward_train(i)
+    dU = torch.empty(M, Fs, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, H, dtype=torch.float32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    dW1t0 = torch.randn(F, H, generator=g, device="cuda")
+    db10 = torch.randn(F, generator=g, device="cuda")
+    dW2t0 = torch.randn(H, F, generator=g, device="cuda")
+    dW1t, db1, dW2t = dW1t0.clone(), db10.clone(), dW2t0.clone()
+    tp.tp_mlp_shard_bwd(p.dX_, p.dW1t, p.dW2t, U, Y, p.ddZ, dU, dX, dW1t, db1, dW2t, M, H, F, T, i,
+                        flags=tp.TP_GRAD_ACCUMULATE)
+    torch.cuda.synchronize()
+    cols = inputs.row_sample(Fs, 12, seed=9)
+    gcols = i * Fs + cols
+    oc = oracle.mlp_shard_bwd(p.X.f64, p.W1.f64[:, gcols], p.b1.f64[gcols], p.W2.f64[gcols], p.dZ.f64, 1, 0)
+    e = (rel_fro(to_f64(dW1t - dW1t0)[gcols].T, oc["dW1_i"]), rel_fro(to_f64(db1 - db10)[gcols], oc["db1_i"]),
+         rel_fro(to_f64(dW2t - dW2t0)[:, gcols].T, oc["dW2_i"]))
+    print("  accumulated columns: dW1 %.2e db1 %.2e dW2 %.2e" % e)
+    assert max(e) <= TOL["bf16"]
+    assert torch.equal(dW1t[:i * Fs], dW1t0[:i * Fs]) and torch.equal(db1[:i * Fs], db10[:i * Fs])
+    assert torch.equal(dW2t[:, :i * Fs], dW2t0[:, :i * Fs])
+
+
 @pytest.mark.parametrize("T,M", [(4, 256), (2, 130)])
 def test_group_entry_points(T, M):
     # the whole group's training forward and backward, one launch per
