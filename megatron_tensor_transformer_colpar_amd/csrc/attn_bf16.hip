@@ -24,12 +24,13 @@
 //   attention recurrence (Dao et al., arXiv:2205.14135).
 // * attn_decode_kernel (a few rows: decode), memory-bound: the keys of a
 //   sequence are split into chunks spread over many workgroups; each streams
-//   its chunk of K and then of V once (the V rows of its first 64 keys
-//   requested with their K rows), 16 lanes per 256-byte row, and writes
-//   an unnormalised partial (max, sum, weighted values).  Each workgroup then
-//   counts its arrival for its (sequence, key/value head); the last to
-//   arrive merges the chunks of those query rows in chunk order and resets
-//   the counter, so the decode step is one launch and no workgroup waits.
+//   its chunk of K and then of V once (the V rows of its first pass of
+//   64 or 128 keys requested with their K rows), 16 lanes per 256-byte row,
+//   and writes an unnormalised partial (max, sum, weighted values).  Each
+//   workgroup then counts its arrival for its (sequence, key/value head);
+//   the last to arrive merges the chunks of those query rows in chunk order
+//   and resets the counter, so the decode step is one launch and no
+//   workgroup waits.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -342,7 +343,7 @@ __device__ __forceinline__ float fetch(const float *p)
 // hold row k of the wave's 4, 16 bytes (8 dims) each.
 // Partial of row r, chunk c: max m, sum l = sum_t 2^(x_t - m), o[d] =
 // sum_t 2^(x_t - m) v_t[d], x_t the scaled score in log2 units.
-template <int NR>
+template <int NR, int UR>
 __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, int nsplit, float *ws_o, float *ws_ml,
                                                           unsigned *arrivals)
 {
@@ -384,30 +385,28 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, 
         make_rsrc(vb_, nk > 0 ? (uint32_t)(((int64_t)(nk - 1) * a.ldv + kD) * 2) : 0u);
     const uint32_t lane_b = 16u * cc;
 
-    // scores: wave w takes keys 16i + 4w + kk, four rows in flight per lane.
-    // The value rows of the first 64 keys do not depend on the scores: they
-    // are requested right behind their key rows and stream under the scores
-    // and the softmax (one sequence in 64-key chunks: 12.53 -> 11.89 us,
-    // bitwise equal; 8 and 32 sequences unchanged).  Requesting the next 64
-    // keys' values as well was slower (11.95 against 11.46 us in 128-key
-    // chunks).
-    u32x4 vfirst[4];
-    for (int base = 0; base < nk; base += 64) {
-        u32x4 kr[4];
+    // scores: wave w takes keys 16i + 4w + kk, UR rows in flight per lane.
+    // The value rows of the first pass's keys do not depend on the scores:
+    // they are requested right behind their key rows and stream under the
+    // scores and the softmax (one sequence in 64-key chunks: 12.53 -> 11.89
+    // us, bitwise equal; 8 and 32 sequences unchanged).
+    u32x4 vfirst[UR];
+    for (int base = 0; base < nk; base += 16 * UR) {
+        u32x4 kr[UR];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < UR; ++u) {
             const int t = base + 16 * u + 4 * wave + kk;
             kr[u] = buf_load16(rk, (uint32_t)(t * a.ldk * 2) + lane_b, 0);
         }
         if (base == 0) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < UR; ++u) {
                 const int t = 16 * u + 4 * wave + kk;
                 vfirst[u] = buf_load16(rv, (uint32_t)(t * a.ldv * 2) + lane_b, 0);
             }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < UR; ++u) {
             const int t = base + 16 * u + 4 * wave + kk;
             float kf[8];
             bf16x8_to_f32(kr[u], kf);
@@ -453,15 +452,15 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnDev a, int chunk, 
     for (int r = 0; r < NR; ++r)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[r][e] = 0.0f;
-    for (int base = 0; base < nk; base += 64) {
-        u32x4 vr[4];
+    for (int base = 0; base < nk; base += 16 * UR) {
+        u32x4 vr[UR];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < UR; ++u) {
             const int t = base + 16 * u + 4 * wave + kk;
             vr[u] = base == 0 ? vfirst[u] : buf_load16(rv, (uint32_t)(t * a.ldv * 2) + lane_b, 0);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < UR; ++u) {
             const int t = base + 16 * u + 4 * wave + kk;
             if (t < nk) {
                 float vf[8];
@@ -578,7 +577,16 @@ hipError_t launch_decode(const AttnDev &d, int chunk, int nsplit, float *ws_o, f
                          hipStream_t s)
 {
     const int grid = d.Bs * d.nkv * nsplit;
-    hipLaunchKernelGGL((attn_decode_kernel<NR>), dim3(grid), dim3(256), 0, s, d, chunk, nsplit, ws_o, ws_ml,
+    // A chunk of at most 128 keys goes in one pass of 8 key rows per lane
+    // (its values requested with it); longer chunks in passes of 4.  One
+    // sequence (16 chunks of 128): 11.47 -> 10.29 us, 8 sequences 21.02 ->
+    // 20.55 us; 32 sequences (chunks of 512) took 57.0 against 53.9 us with 8
+    // rows.  Bitwise equal: a lane visits the same keys in the same order.
+    if (chunk <= 128)
+        hipLaunchKernelGGL((attn_decode_kernel<NR, 8>), dim3(grid), dim3(256), 0, s, d, chunk, nsplit, ws_o, ws_ml,
+                           arrivals);
+    else
+        hipLaunchKernelGGL((attn_decode_kernel<NR, 4>), dim3(grid), dim3(256), 0, s, d, chunk, nsplit, ws_o, ws_ml,
                        arrivals);
     return hipGetLastError();
 }
