@@ -340,7 +340,8 @@ __device__ __forceinline__ float fetch(const float *p)
 // Workgroup (b, g, c): keys [c*chunk, (c+1)*chunk) of sequence b against the
 // NR = G*Sq query rows that read key/value head g (row r = gq*Sq + s is query
 // s of head g*G + gq).  Lane layout over a K or V row: lanes 16k .. 16k+15
-// hold row k of the wave's 4, 16 bytes (8 dims) each.
+// hold row k of the wave's 4, 16 bytes (8 dims) each; a pass over the chunk
+// takes 16*UR keys, UR rows in flight per lane.
 // Partial of row r, chunk c: max m, sum l = sum_t 2^(x_t - m), o[d] =
 // sum_t 2^(x_t - m) v_t[d], x_t the scaled score in log2 units.
 template <int NR, int UR>
